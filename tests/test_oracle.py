@@ -1,0 +1,437 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself:
+the pages' worked example, closed forms, library routines, brute force over
+tiny inputs and invariants.  CPU only."""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import fathom, select, hamming, quest, attend
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _bf16(x):
+    return synth.f32_to_bf16_bits(np.asarray(x, np.float32))
+
+
+# ---------------------------------------------------------------- Hamming
+def _read_golden(name):
+    rec = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, *v = line.split()
+            rec[k] = v
+    return rec
+
+
+def test_hamming_worked_example():
+    rec = _read_golden("hamming_worked_example.txt")
+    q = int(rec["query"][0], 2)
+    keys = np.array([int(s, 2) for s in rec["keys"]], np.uint32)
+    dist = hamming.distances(keys, q)
+    assert [int(x) for x in dist] == [int(s) for s in rec["distances"]]
+    assert [int(np.uint32(k) ^ np.uint32(q)) for k in keys] == [int(s, 2) for s in rec["xor"]]
+    sel = select.topk(dist, int(rec["budget"][0]), largest=False)
+    assert list(sel) == [int(s) for s in rec["selected"]]
+
+
+def test_hamming_brute_force():
+    g = np.random.default_rng(5)
+    sigs = g.integers(0, 1 << 32, size=(3, 257), dtype=np.uint64).astype(np.uint32)
+    qs = g.integers(0, 1 << 32, size=3, dtype=np.uint64).astype(np.uint32)
+    d = hamming.distances_heads(sigs, qs)
+    for h in range(3):
+        for i in range(257):
+            assert d[h, i] == bin(int(sigs[h, i]) ^ int(qs[h])).count("1")
+    assert hamming.distances(np.uint32(0xFFFFFFFF), np.uint32(0)) == 32
+
+
+# ---------------------------------------------------------------- top-k
+def _topk_brute(keys, k, largest, n_sink, n_local):
+    n = len(keys)
+    comp = list(range(n_sink, n - n_local))
+    sgn = -1 if largest else 1
+    comp.sort(key=lambda i: (sgn * float(keys[i]), i))
+    chosen = sorted(comp[:k])
+    return list(range(n_sink)) + chosen + list(range(n - n_local, n))
+
+
+@pytest.mark.parametrize("largest", [True, False])
+def test_topk_brute(largest):
+    g = np.random.default_rng(11)
+    for trial in range(40):
+        n = int(g.integers(1, 90))
+        n_sink = int(g.integers(0, 4)) if n > 8 else 0
+        n_local = int(g.integers(0, 4)) if n > 8 else 0
+        k = int(g.integers(0, n + 2))
+        if largest:
+            keys = g.integers(-3, 4, size=n).astype(np.float32) * np.float32(0.5)   # many ties
+        else:
+            keys = g.integers(0, 6, size=n).astype(np.uint8)
+        got = list(select.topk(keys, k, largest, n_sink, n_local))
+        assert got == _topk_brute(keys, k, largest, n_sink, n_local)
+
+
+def test_topk_special_cases():
+    assert list(select.topk(np.zeros(10, np.float32), 4)) == [0, 1, 2, 3]
+    x = np.arange(7, dtype=np.float32)
+    assert list(select.topk(x, 7)) == list(range(7))
+    assert list(select.topk(x, 100)) == list(range(7))
+    assert list(select.topk(np.array([0.0, -0.0, 0.0], np.float32), 1)) == [0]
+    assert list(select.topk(np.array([-0.0, 0.0], np.float32), 1)) == [0]
+    # window accounting of the notes' budget example: 16,384 tokens, 16x
+    # sparsity (1,024 retrieved) plus 128 sink and 128 local = 1,280 rows
+    n = 16384
+    keys = np.random.default_rng(1).standard_normal(n).astype(np.float32)
+    out = select.topk(keys, n // 16, True, 128, 128)
+    assert len(out) == 1280 and len(set(out.tolist())) == 1280
+    assert abs(len(out) / n - 0.0781) < 5e-5
+
+
+# ---------------------------------------------------------------- quantiser / planes
+def _keys(n, d, seed=0, sig=None):
+    g = np.random.default_rng(seed)
+    sig = g.uniform(0.05, 4.0, d) if sig is None else sig
+    return _bf16(g.standard_normal((n, d)) * sig)
+
+
+def test_plane_layout_by_hand():
+    codes = np.zeros((64, 2), np.uint8)
+    codes[0, 0] = 8          # MSB only -> plane 0, token 0 -> word 0 bit 0
+    codes[33, 0] = 1         # LSB only -> plane 3, token 33 -> word 1 bit 1
+    codes[5, 1] = 15         # all planes, token 5 -> word 0 bit 5
+    pl = fathom.pack_planes(codes)
+    assert pl.shape == (2, 4, 2)
+    assert pl[0, 0, 0] == 1 and pl[0, 0, 1] == 0
+    assert pl[0, 3, 1] == 2 and pl[0, 3, 0] == 0
+    assert pl[0, 1].sum() == 0 and pl[0, 2].sum() == 0
+    for p in range(4):
+        assert pl[1, p, 0] == 32 and pl[1, p, 1] == 0
+
+
+def test_meta_layout_by_hand():
+    s = np.array([[1.0, 0.5]], np.float16)
+    o = np.array([[-2.0, 3.0]], np.float16)
+    m = fathom.pack_meta(s, o)
+    assert m.shape == (2, 1)
+    assert m[0, 0] == (0x3C00 | (0xC000 << 16))
+    assert m[1, 0] == (0x3800 | (0x4200 << 16))
+
+
+def test_quantiser_properties():
+    n, d = 256, 16
+    k = _keys(n, d, 3)
+    x = fathom.bf16_bits_to_f32(k).astype(np.float64)
+    codes, scale, offset = fathom.quantise(k)
+    assert codes.max() <= 15
+    blk = np.arange(n) // 64
+    rec = offset.astype(np.float64)[blk] + scale.astype(np.float64)[blk] * codes
+    # every key is within half a step of its reconstruction, up to the fp16
+    # rounding of offset and scale (bounded by 15 half-ulps of the scale)
+    sc = scale.astype(np.float64)[blk]
+    err = np.abs(rec - x)
+    slack = np.abs(offset.astype(np.float64)[blk]) * 2 ** -11 + 16 * sc * 2 ** -11
+    assert np.all(err <= sc / 2 + slack + 1e-12)
+    # each block's extremes land near the ends of the code range
+    cb = codes.reshape(-1, 64, d)
+    assert np.all(cb.min(axis=1) <= 1) and np.all(cb.max(axis=1) >= 14)
+
+
+def test_quantiser_constant_block():
+    k = _bf16(np.full((64, 3), 1.25))
+    codes, scale, offset = fathom.quantise(k)
+    assert np.all(codes == 0) and np.all(scale == 0) and np.all(offset == np.float16(1.25))
+
+
+def test_pack_unpack_roundtrip_and_prefix():
+    n, d = 192, 8
+    k = _keys(n, d, 4)
+    codes, scale, offset = fathom.quantise(k)
+    pl = fathom.pack_planes(codes)
+    for j in range(d):
+        for t in range(5):
+            assert np.array_equal(fathom.prefix_code(pl[j], t, n), codes[:, j].astype(np.int64) >> (4 - t))
+    s, o = fathom.unpack_meta(fathom.pack_meta(scale, offset))
+    assert np.array_equal(s.T.view(np.uint16), scale.view(np.uint16))
+    assert np.array_equal(o.T.view(np.uint16), offset.view(np.uint16))
+
+
+# ---------------------------------------------------------------- plan
+def _objective(w, depth):
+    return sum(float(w[j]) * 4.0 ** (-int(depth[j])) for j in range(len(w)))
+
+
+def test_plan_invariants():
+    g = np.random.default_rng(7)
+    for trial in range(30):
+        d = int(g.integers(1, 40))
+        H = int(g.integers(1, 5))
+        q = g.standard_normal((H, d)).astype(np.float32)
+        var = g.uniform(0.01, 4, d).astype(np.float32)
+        B = int(g.integers(0, 4 * d + 5))
+        depth, qbar = fathom.plan(q, var, B)
+        assert depth.max(initial=0) <= 4
+        assert int(depth.sum()) == min(B, 4 * d)
+        # qbar: float32 sum in head order
+        ref = q[0].copy()
+        for h in range(1, H):
+            ref = ref + q[h]
+        assert np.array_equal(qbar, ref)
+
+
+def test_plan_brute_force_optimal():
+    """For tiny d, the greedy plan minimises sum_j w_j 4^-t_j over every
+    allocation with the same total (reverse water-filling optimality)."""
+    g = np.random.default_rng(8)
+    for trial in range(25):
+        d = int(g.integers(1, 6))
+        q = g.standard_normal((2, d)).astype(np.float32)
+        var = g.uniform(0.05, 4, d).astype(np.float32)
+        B = int(g.integers(0, 4 * d + 1))
+        depth, qbar = fathom.plan(q, var, B)
+        w = (qbar.astype(np.float64) ** 2) * var
+        best = min(_objective(w, a) for a in itertools.product(range(5), repeat=d) if sum(a) == B)
+        assert _objective(w, depth) <= best * (1 + 1e-6) + 1e-30
+
+
+def test_plan_special_cases():
+    d = 6
+    var = np.ones(d, np.float32)
+    q = np.ones((1, d), np.float32)
+    assert fathom.plan(q, var, 0)[0].sum() == 0
+    assert np.all(fathom.plan(q, var, 4 * d)[0] == 4)
+    assert np.all(fathom.plan(q, var, 4 * d + 9)[0] == 4)
+    # all weights equal, B = d: one bit per channel (gain 1 beats 1/4)
+    assert np.all(fathom.plan(q, var, d)[0] == 1)
+    # equal weights, B = d + 2: the two lowest channels get the second bit
+    assert list(fathom.plan(q, var, d + 2)[0]) == [2, 2, 1, 1, 1, 1]
+    # one dominant channel (w 1000x) takes all 4 bits before any other
+    q2 = q.copy()
+    q2[0, 3] = 40.0
+    dep = fathom.plan(q2, var, 4)[0]
+    assert dep[3] == 4 and dep.sum() == 4
+    # a channel 16x heavier: its third bit (gain 16/16) ties with the other
+    # channels' first bits, and ties go to the lower channel
+    q3 = np.ones((1, 3), np.float32)
+    q3[0, 2] = 4.0
+    assert list(fathom.plan(q3, np.ones(3, np.float32), 4)[0]) == [1, 1, 2]
+    assert list(fathom.plan(q3, np.ones(3, np.float32), 5)[0]) == [1, 1, 3]
+
+
+def test_plan_water_level():
+    """With theta the smallest taken gain, every channel holds exactly the
+    bits whose gain exceeds theta, plus tied bits in (j, t) order."""
+    g = np.random.default_rng(9)
+    q = g.standard_normal((4, 128)).astype(np.float32)
+    var = g.uniform(0.0025, 16, 128).astype(np.float32)
+    depth, qbar = fathom.plan(q, var, 56)
+    w = fathom.channel_weight(qbar, var).astype(np.float64)
+    gains = [(w[j] * 4.0 ** -t, j, t) for j in range(128) for t in range(depth[j])]
+    theta = min(x[0] for x in gains)
+    for j in range(128):
+        above = sum(1 for t in range(4) if w[j] * 4.0 ** -t > theta)
+        assert depth[j] >= above
+        assert depth[j] <= sum(1 for t in range(4) if w[j] * 4.0 ** -t >= theta)
+    # with real-valued gains the plan's statistic is what the page describes
+    # for 48 bits: roughly a quarter of the 128 channels are touched
+    d48, _ = fathom.plan(q, var, 48)
+    assert 16 <= int((d48 > 0).sum()) <= 48
+
+
+def test_plan_uniform():
+    g = np.random.default_rng(10)
+    q = g.standard_normal((4, 128)).astype(np.float32)
+    var = g.uniform(0.01, 4, 128).astype(np.float32)
+    dep, qbar = fathom.plan_uniform(q, var, 34)
+    assert int((dep == 4).sum()) == 34 and int(dep.sum()) == 136
+    w = fathom.channel_weight(qbar, var)
+    assert w[dep == 4].min() >= w[dep == 0].max()
+
+
+# ---------------------------------------------------------------- scan
+def test_scan_full_plan_equals_dequantised_dot():
+    """B = 4d: the scan equals qbar . (offset + scale * code) with the codes
+    taken straight from the quantiser (not from the planes)."""
+    n, d = 256, 128
+    k = _keys(n, d, 12)
+    codes, scale, offset = fathom.quantise(k)
+    pl = fathom.pack_planes(codes)
+    meta = fathom.pack_meta(scale, offset)
+    q = np.random.default_rng(13).standard_normal((4, d)).astype(np.float32)
+    var = np.ones(d, np.float32)
+    depth, qbar = fathom.plan(q, var, 4 * d)
+    s = fathom.scan(pl, meta, depth, qbar, n)
+    blk = np.arange(n) // 64
+    deq = offset.astype(np.float64)[blk] + scale.astype(np.float64)[blk] * codes
+    ref = deq @ qbar.astype(np.float64)
+    assert np.allclose(s, ref, rtol=1e-12, atol=1e-9)
+    # and it approximates the exact bf16 dot product within the quantiser's error
+    exact = fathom.bf16_bits_to_f32(k).astype(np.float64) @ qbar.astype(np.float64)
+    bound = (np.abs(qbar.astype(np.float64))[None, :] * (scale.astype(np.float64)[blk] * 0.51 + 1e-3)).sum(1)
+    assert np.all(np.abs(s - exact) <= bound)
+
+
+def test_scan_partial_depth_brute_force():
+    """Tiny n: each read channel contributes qbar_j times the mean of the
+    4-bit code values sharing the token's t-bit prefix (the midpoint of the
+    t-bit bin under the same block scale), computed token by token."""
+    n, d = 128, 6
+    k = _keys(n, d, 14)
+    codes, scale, offset = fathom.quantise(k)
+    pl = fathom.pack_planes(codes)
+    meta = fathom.pack_meta(scale, offset)
+    g = np.random.default_rng(15)
+    for trial in range(10):
+        depth = g.integers(0, 5, size=d).astype(np.uint8)
+        qbar = g.standard_normal(d).astype(np.float32)
+        s = fathom.scan(pl, meta, depth, qbar, n)
+        for i in range(n):
+            b = i // 64
+            tot = 0.0
+            for j in range(d):
+                t = int(depth[j])
+                if t == 0:
+                    continue
+                prefix = int(codes[i, j]) >> (4 - t)
+                members = [c for c in range(16) if c >> (4 - t) == prefix]
+                tot += float(qbar[j]) * (float(offset[b, j]) + float(scale[b, j]) * (sum(members) / len(members)))
+            assert math.isclose(s[i], tot, rel_tol=1e-12, abs_tol=1e-9)
+
+
+def test_scan_single_channel_closed_form():
+    n, d = 64, 4
+    k = _keys(n, d, 16)
+    codes, scale, offset = fathom.quantise(k)
+    pl = fathom.pack_planes(codes)
+    meta = fathom.pack_meta(scale, offset)
+    qbar = np.zeros(d, np.float32)
+    qbar[2] = 2.5
+    depth = np.array([0, 0, 4, 0], np.uint8)
+    s = fathom.scan(pl, meta, depth, qbar, n)
+    ref = 2.5 * (float(offset[0, 2]) + float(scale[0, 2]) * codes[:, 2].astype(np.float64))
+    assert np.allclose(s, ref, rtol=0, atol=1e-12)
+    depth = np.array([0, 0, 1, 0], np.uint8)
+    s1 = fathom.scan(pl, meta, depth, qbar, n)
+    hi = codes[:, 2] >= 8
+    ref1 = 2.5 * (float(offset[0, 2]) + float(scale[0, 2]) * np.where(hi, 11.5, 3.5))
+    assert np.allclose(s1, ref1, rtol=0, atol=1e-12)
+
+
+def test_needles_found_at_56_bits():
+    """End-to-end sanity on the 32k GQA layer's shape (shortened to 8k
+    tokens, two KV heads): every planted needle is in the top-512."""
+    case = synth.fathom_case(2, n=8192, heads=[0, 1], with_values=False)
+    for hi, g in enumerate(case["heads"]):
+        codes, scale, offset = fathom.quantise(case["K"][hi])
+        pl = fathom.pack_planes(codes)
+        meta = fathom.pack_meta(scale, offset)
+        qg = case["q"][g * 4:(g + 1) * 4]
+        depth, qbar = fathom.plan(qg, case["var"][g], 56)
+        s = fathom.scan(pl, meta, depth, qbar, case["n"])
+        top = set(select.topk(s, 512).tolist())
+        assert set(case["needle_pos"][hi].tolist()) <= top
+
+
+# ---------------------------------------------------------------- Quest summaries
+def test_quest_bound_and_rounding():
+    g = np.random.default_rng(17)
+    n, d = 256, 128
+    sig = np.exp(g.uniform(np.log(0.05), np.log(4), d))
+    k = _bf16(g.standard_normal((n, d)) * sig)
+    # include values that fp16 cannot hold exactly (tiny magnitudes)
+    k[3, :5] = _bf16(np.array([1e-7, -3e-6, 2e-5, -1e-8, 7e-6]))
+    x = fathom.bf16_bits_to_f32(k).astype(np.float64)
+    mn, mx = quest.summaries(k, 16)
+    xb = x.reshape(-1, 16, d)
+    assert np.all(mn.astype(np.float64) <= xb.min(1)) and np.all(mx.astype(np.float64) >= xb.max(1))
+    q = g.standard_normal((4, d)).astype(np.float32)
+    S = quest.block_scores(mn, mx, q)
+    for b in range(n // 16):
+        for h in range(4):
+            sh = quest.block_scores(mn[b:b + 1], mx[b:b + 1], q[h:h + 1])[0]
+            assert sh >= (xb[b] @ q[h].astype(np.float64)).max() - 1e-9
+        # the group score is the sum of the heads' bounds, brute force
+        ref = sum(max(float(q[h, j]) * float(mn[b, j]), float(q[h, j]) * float(mx[b, j]))
+                  for h in range(4) for j in range(d))
+        assert math.isclose(S[b], ref, rel_tol=1e-12, abs_tol=1e-9)
+
+
+def test_quest_exact_when_representable():
+    k = _bf16(np.array([[1.0, -2.0], [0.5, 3.0]] * 8))
+    mn, mx = quest.summaries(k, 16)
+    assert list(mn[0]) == [0.5, -2.0] and list(mx[0]) == [1.0, 3.0]
+
+
+# ---------------------------------------------------------------- attention
+def _dense_sdpa(q, Kb, Vb):
+    """Dense attention through torch's own SDPA in float64 on the CPU."""
+    K = torch.from_numpy(attend.bf16_bits_to_f64(Kb))[None, None]
+    V = torch.from_numpy(attend.bf16_bits_to_f64(Vb))[None, None]
+    Q = torch.from_numpy(np.asarray(q, np.float64))[None, None, None]
+    return torch.nn.functional.scaled_dot_product_attention(Q, K, V)[0, 0, 0].numpy()
+
+
+def test_sparse_with_all_rows_equals_dense():
+    g = np.random.default_rng(19)
+    n, d = 300, 128
+    Kb = _bf16(g.standard_normal((n, d)) * 2)
+    Vb = _bf16(g.standard_normal((n, d)))
+    q = g.standard_normal(d).astype(np.float32)
+    o = attend.attend_rows(q, Kb, Vb, 1 / math.sqrt(d))
+    assert np.allclose(o, _dense_sdpa(q, Kb, Vb), rtol=1e-10, atol=1e-12)
+
+
+def test_attend_batched_and_special_cases():
+    g = np.random.default_rng(20)
+    R, Hq, Hkv, n, d = 2, 4, 2, 96, 128
+    K = _bf16(g.standard_normal((R, Hkv, n, d))).reshape(R, Hkv, n, d)
+    V = _bf16(g.standard_normal((R, Hkv, n, d))).reshape(R, Hkv, n, d)
+    q = g.standard_normal((R, Hq, d)).astype(np.float32)
+    idx = np.stack([np.stack([np.sort(g.choice(n, 17, replace=False)) for _ in range(Hkv)]) for _ in range(R)])
+    o = attend.attend(q, K, V, idx)
+    for r in range(R):
+        for h in range(Hq):
+            sel = idx[r, h // 2]
+            ref = _dense_sdpa(q[r, h], K[r, h // 2, sel], V[r, h // 2, sel])
+            assert np.allclose(o[r, h], ref, rtol=1e-10, atol=1e-12)
+    # a single selected row returns its value row
+    one = attend.attend(q, K, V, idx[:, :, :1])
+    assert np.allclose(one[0, 0], attend.bf16_bits_to_f64(V[0, 0, idx[0, 0, 0]]))
+    # equal logits (identical keys) give the mean of the selected values
+    K2 = K.copy()
+    K2[:, :, :, :] = K[0, 0, 0]
+    o2 = attend.attend(q, K2, V, idx)
+    assert np.allclose(o2[1, 3], attend.bf16_bits_to_f64(V[1, 1, idx[1, 1]]).mean(0))
+    # block ids of 16 rows equal the same rows listed one by one
+    bids = np.array([[[0, 5], [2, 3]]] * R)
+    ob = attend.attend(q, K, V, bids, block_tokens=16)
+    rows = quest.expand_blocks(bids.reshape(-1, 2)[0], 16)
+    assert np.allclose(ob[0, 0], attend.attend_rows(q[0, 0], K[0, 0, rows], V[0, 0, rows], 1 / math.sqrt(d)))
+
+
+# ---------------------------------------------------------------- byte model
+def test_byte_model_against_pages():
+    from sparse_top_decode_query_amd import bytemodel as bm
+    layers, kvh, d = 36, 8, 128        # Qwen3-8B's depth and KV heads
+    # dense attention at 32k reads about 4.8 GB per step
+    assert abs(bm.kv_cache_bytes(1, 32768, layers, kvh, d) / 1e9 - 4.8) < 0.05
+    # a 136-bit scan index: 160 MB at 32k, 5.1 GB at 1M tokens
+    assert abs(bm.uniform_index_bytes(32768, layers, kvh, 136) / 1e6 - 160) < 1.0
+    assert abs(bm.uniform_index_bytes(1 << 20, layers, kvh, 136) / 1e9 - 5.1) < 0.05
+    # min/max summaries are 1/16 of the KV cache; a signature 1/64 of an fp16 key
+    assert bm.summary_bytes_per_token() * 16 == bm.kv_bytes_per_token()
+    assert 4 * 64 == 128 * 2
+    # 1,024 retrieved + 256 fixed rows of 16,384 is 7.81%
+    assert round(100 * bm.budget_fraction(16384, 1024, 256), 2) == 7.81
+    # the plane scan's read bytes for the uniform plan equal 17 B per token
+    dep = [[4] * 34 + [0] * 94]
+    assert bm.plane_scan_read_bytes(1 << 20, dep) == (1 << 20) * (136 // 8) + 34 * (1 << 14) * 4
