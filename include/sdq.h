@@ -1,0 +1,216 @@
+/*
+ * sdq.h -- C ABI of libsdq.so: one long-context decode step of sparse
+ * attention on an MI355X (gfx950).
+ *
+ * The step: score every cached key through a cheap index, keep the top-k per
+ * KV head, read those bf16 K/V rows by index and run renormalised softmax
+ * attention over them.  Three index formats are supported:
+ *   - per-channel 4-bit bit planes read under a per-query plan (Fathom
+ *     summary page: bit-plane and reverse water-filling paragraphs),
+ *   - 32-bit signatures scored by XOR/popcount (HashAttention study notes,
+ *     sec. 2.2),
+ *   - per-block min/max key summaries (OasisKV review, Quest-style block
+ *     summaries in the background and core-method sections).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers owned by the caller, unless a comment says
+ *     host.  The library never allocates or frees; scratch memory is a
+ *     caller-supplied workspace whose size the matching *_workspace_bytes()
+ *     returns.
+ *   - Every call is asynchronous on the caller's stream (0 = the null
+ *     stream).  Results are valid once the stream reaches that point.
+ *   - Every call validates its arguments before launching anything; a call
+ *     that returns an error has launched nothing.  Return values:
+ *       SDQ_OK (0), SDQ_EINVAL (-1: null pointer, bad size or shape),
+ *       SDQ_ENOTSUP (-2), SDQ_EHIP (-3: a HIP launch/runtime error).
+ *     sdq_last_error() returns a message for the calling thread's last error.
+ *   - The library holds no global mutable state apart from that per-thread
+ *     message; calls on different streams may run concurrently if their
+ *     output and workspace buffers do not overlap.
+ *   - Head dimension d must be 128 in this version.
+ *   - bf16 and fp16 data are passed as uint16_t bit patterns.
+ */
+#ifndef SDQ_H
+#define SDQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SDQ_OK 0
+#define SDQ_EINVAL (-1)
+#define SDQ_ENOTSUP (-2)
+#define SDQ_EHIP (-3)
+
+/* key kinds for topk_select */
+#define SDQ_KEY_F32_MAX 0 /* float32 scores, largest first        */
+#define SDQ_KEY_U8_MIN 1  /* uint8 distances, smallest first      */
+
+/* Message describing the calling thread's most recent error ("" if none). */
+const char* sdq_last_error(void);
+
+/* ABI version of this header (incremented on incompatible changes). */
+int sdq_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * Index construction (the step before the decode path)
+ * --------------------------------------------------------------------- */
+
+/* fathom_ingest -- build the bit-plane index of a bf16 key cache.
+ * Fathom summary, bit-plane paragraph: keys are quantised per channel to
+ * 4-bit uniform codes with one fp16 scale per 64-token block, and each code
+ * bit is stored as its own channel-major plane.
+ *   keys    bf16 [G][n][d]   key cache, token-major rows
+ *   planes  uint32 [G][d][4][n/32]  out.  Plane p holds code bit (3-p), so
+ *           plane 0 is the MSB and a channel's first t planes form one
+ *           contiguous range of t*n/8 bytes.  Token i is bit (i & 31) of
+ *           word (i >> 5).
+ *   meta    uint32 [G][d][n/64]  out.  Low half: fp16 scale; high half:
+ *           fp16 offset of that channel's 64-token block.
+ * Quantiser (float32): offset = fp16(min), scale = fp16((max-min)/15),
+ * code = clamp(rint((x - offset)/scale), 0, 15), code 0 where scale is 0.
+ * Keys must be finite and within fp16 range.
+ * Errors: SDQ_EINVAL if a pointer is null, G < 1, n < 64, n % 64 != 0 or
+ * d != 128. */
+int fathom_ingest(const uint16_t* keys, int G, int n, int d, uint32_t* planes, uint32_t* meta,
+                  hipStream_t stream);
+
+/* minmax_summarize -- per-block min/max key summaries (OasisKV review,
+ * Quest-style summaries: one minimum and one maximum vector per logical
+ * block, per dimension).
+ *   keys  bf16 [RG][n][d];   bmin, bmax  fp16 [RG][n/block][d]  out.
+ * The block minimum is rounded to fp16 downwards and the maximum upwards, so
+ * each summary still bounds every key of its block.
+ * Errors: SDQ_EINVAL on null pointers, RG < 1, block < 1, n % block != 0,
+ * d != 128. */
+int minmax_summarize(const uint16_t* keys, int RG, int n, int d, int block, uint16_t* bmin,
+                     uint16_t* bmax, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Decode step
+ * --------------------------------------------------------------------- */
+
+/* fathom_plan -- per-query read plan by reverse water-filling.
+ * Fathom summary, water-filling paragraph: channel j contributes
+ * q_j^2 * var_j to the score variance, each extra bit cuts the remaining
+ * error of that channel by 4, and budget_bits plane bits are spread over the
+ * channels (0..4 each) by this marginal gain; query heads under one KV head
+ * share one plan.
+ *   q        float32 [G*H_grp][d]  query rows; rows g*H_grp..g*H_grp+H_grp-1
+ *            belong to KV head g
+ *   key_var  float32 [G][d]        calibrated key variance per channel (>= 0)
+ *   depth    uint8 [G][d]   out: bits to read per channel (0..4)
+ *   qbar     float32 [G][d] out: the group's query sum, added in head order
+ * Exactly min(budget_bits, 4d) bits are given out per KV head: the items
+ * w_j * 4^-t (w_j = (qbar_j*qbar_j)*var_j, float32) are taken in the order
+ * (gain desc, channel asc, bit asc).
+ * Errors: SDQ_EINVAL on null pointers, G < 1, H_grp < 1, d != 128,
+ * budget_bits < 0. */
+int fathom_plan(const float* q, const float* key_var, int G, int H_grp, int d, int budget_bits,
+                uint8_t* depth, float* qbar, hipStream_t stream);
+
+/* fathom_plan_uniform -- the uniform-depth baseline plan the Fathom summary
+ * compares against (a fixed set of channels read at full depth): the
+ * n_channels channels of largest (qbar_j*qbar_j)*var_j, ties to the lower
+ * channel, each at depth 4.  Same arguments and errors as fathom_plan with
+ * 0 <= n_channels <= d in place of the budget. */
+int fathom_plan_uniform(const float* q, const float* key_var, int G, int H_grp, int d,
+                        int n_channels, uint8_t* depth, float* qbar, hipStream_t stream);
+
+/* fathom_gather -- copy the active channels' plane prefixes from host memory
+ * into HBM (Fathom summary, offload paragraph: host planes are contiguous
+ * per channel and one gather moves the active prefixes over PCIe before the
+ * scan).
+ *   planes_host, meta_host  HOST pointers to pinned, device-mapped memory
+ *           (hipHostMalloc) in the fathom_ingest layout
+ *   depth   uint8 [G][d] device, a plan from fathom_plan*
+ *   planes_dev, meta_dev  device buffers in the same layout; for every
+ *           channel with depth t > 0 the first t planes and the meta row are
+ *           written, everything else is left untouched.
+ * Run it on a side stream ordered after the plan with events.
+ * Errors: SDQ_EINVAL on null pointers, bad sizes (as fathom_ingest), or host
+ * memory the device cannot address. */
+int fathom_gather(const uint32_t* planes_host, const uint32_t* meta_host, const uint8_t* depth,
+                  int G, int d, int n, uint32_t* planes_dev, uint32_t* meta_dev,
+                  hipStream_t stream);
+
+/* fathom_scan -- approximate scores from the plane prefixes.
+ * For every KV head g and token i:
+ *   s[g][i] = sum over channels j with t_j = depth[g][j] > 0 of
+ *             qbar[g][j] * (offset + scale * (c * 2^(4-t_j) + (2^(4-t_j)-1)/2))
+ * where c is the t_j-bit code read from the first t_j planes and scale/offset
+ * are that channel's 64-token block metadata (the midpoint of the t-bit bin,
+ * the 4-bit dequantisation at t = 4).  Unread channels contribute nothing and
+ * their metadata is not read.  Accumulation is float32.
+ *   planes, meta  as fathom_ingest;  depth, qbar as fathom_plan
+ *   scores        float32 [G][n] out
+ * Errors: SDQ_EINVAL on null pointers, G < 1, n < 64, n % 64 != 0, d != 128. */
+int fathom_scan(const uint32_t* planes, const uint32_t* meta, const uint8_t* depth,
+                const float* qbar, int G, int d, int n, float* scores, hipStream_t stream);
+
+/* topk_select -- per-row top-k (HashAttention study notes, sec. 2.1 TOPK and
+ * sec. 3.1 fixed positions; OasisKV review, per-KV-head top-K).
+ *   keys      [rows][n]: float32 (SDQ_KEY_F32_MAX, largest first; must be
+ *             finite, -0 equals +0) or uint8 (SDQ_KEY_U8_MIN, smallest first)
+ *   idx_out   int32 [rows][k + n_sink + n_local] out
+ * Per row: positions [0, n_sink) and [n - n_local, n) are always kept and do
+ * not compete; the k best of [n_sink, n - n_local) are added, equal keys
+ * going to the lower index.  Indices are written in ascending order.  When k
+ * is at least n - n_sink - n_local every index 0..n-1 is written and the
+ * rest of the row is filled with -1.
+ *   ws, ws_bytes  workspace of at least topk_select_workspace_bytes() bytes
+ * Errors: SDQ_EINVAL on null pointers, rows < 1, n < 1, k < 0, n_sink < 0,
+ * n_local < 0, n_sink + n_local > n, unknown key_type, short workspace. */
+size_t topk_select_workspace_bytes(int rows, int n, int k, int key_type);
+int topk_select(const void* keys, int key_type, int rows, int n, int k, int n_sink, int n_local,
+                int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* hamming_scan -- dist[h][i] = popcount(sigs[h][i] XOR qsig[h]) in [0, 32]
+ * (HashAttention study notes, sec. 2.2).
+ *   sigs uint32 [H][n];  qsig uint32 [H];  dist uint8 [H][n] out
+ * Errors: SDQ_EINVAL on null pointers, H < 1, n < 1. */
+int hamming_scan(const uint32_t* sigs, const uint32_t* qsig, int H, int n, uint8_t* dist,
+                 hipStream_t stream);
+
+/* minmax_block_scan -- block scores against min/max summaries (OasisKV
+ * review, Quest-style summaries):
+ *   S[rg][b] = sum over the group's heads h and dims j of
+ *              max(q[h][j] * bmin[rg][b][j], q[h][j] * bmax[rg][b][j])
+ *   bmin, bmax fp16 [RG][nb][d];  q float32 [RG*H_grp][d];  S float32 [RG][nb] out
+ * Errors: SDQ_EINVAL on null pointers, RG < 1, H_grp < 1, nb < 1, d != 128. */
+int minmax_block_scan(const uint16_t* bmin, const uint16_t* bmax, const float* q, int RG, int H_grp,
+                      int nb, int d, float* block_scores, hipStream_t stream);
+
+/* gather_attend -- renormalised softmax attention over selected rows read by
+ * index (HashAttention study notes, sec. 2.1 sparse output formula and
+ * sec. 2.5 page-size-one reads):
+ *   o[r][h] = sum_{i in I} e^{z_i} v_i / sum_{i in I} e^{z_i},
+ *   z_i = softmax_scale * <q[r][h], K[r][kvh][i]>,  kvh = h / (H_q / H_kv)
+ *   q     float32 [R][H_q][d]
+ *   K, V  bf16 [R][H_kv][n][d]
+ *   idx   int32 [R][H_sel][n_idx], H_sel = H_q if sets_per_query_head else
+ *         H_kv (then the H_q/H_kv query heads of a group share the set).
+ *         With block_tokens == 1 an entry is a row; with block_tokens > 1 it
+ *         is a block id covering rows [b*block_tokens, (b+1)*block_tokens).
+ *         Negative entries are padding and are skipped; entries must be
+ *         distinct, and entries past the cache end are skipped as well.
+ *   out   float32 [R][H_q][d]; a set with no valid entry yields zeros.
+ *   ws, ws_bytes  workspace of at least gather_attend_workspace_bytes() bytes
+ * Errors: SDQ_EINVAL on null pointers, R, H_q, H_kv, n, n_idx, block_tokens
+ * < 1, H_q % H_kv != 0, d != 128, short workspace. */
+size_t gather_attend_workspace_bytes(int R, int H_q, int H_kv, int sets_per_query_head, int n_idx,
+                                     int block_tokens, int d);
+int gather_attend(const float* q, const uint16_t* K, const uint16_t* V, const int32_t* idx, int R,
+                  int H_q, int H_kv, int sets_per_query_head, int n, int n_idx, int block_tokens,
+                  int d, float softmax_scale, float* out, void* ws, size_t ws_bytes,
+                  hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDQ_H */

@@ -1,0 +1,123 @@
+// Per-query read plan by reverse water-filling (Fathom summary,
+// water-filling paragraph): one wavefront per KV head.
+//
+// The 4d candidate bits (channel j, bit t) have gain v(j,t) = w_j * 4^-t with
+// w_j = (qbar_j * qbar_j) * var_j, qbar the float32 sum of the group's query
+// rows in head order.  The plan takes the first min(B, 4d) bits in the order
+// (gain desc, j asc, t asc).  Lane l owns channels l and l+64 (8 candidate
+// bits); the B-th largest gain T is found by a 31-step bitwise search over the
+// gains' bit patterns (non-negative floats order like their bit patterns),
+// counting candidates with wave ballots.  Bits with gain > T are taken, and of
+// the bits with gain == T the first B - #(gain > T) in (j, t) order.
+#include "common.hpp"
+
+namespace sdq {
+
+__device__ __forceinline__ int wave_count(bool p) { return __popcll(__ballot(p)); }
+
+template <bool UNIFORM>
+__global__ __launch_bounds__(64) void fathom_plan_kernel(const float* __restrict__ q,
+                                                         const float* __restrict__ var, int Hgrp,
+                                                         int budget, uint8_t* __restrict__ depth,
+                                                         float* __restrict__ qbar) {
+  const int g = blockIdx.x;
+  const int l = threadIdx.x;
+  const int j0 = l, j1 = l + 64;
+  const float* qg = q + size_t(g) * Hgrp * kHeadDim;
+  float a0 = qg[j0], a1 = qg[j1];
+  for (int h = 1; h < Hgrp; ++h) {
+    a0 = __fadd_rn(a0, qg[size_t(h) * kHeadDim + j0]);
+    a1 = __fadd_rn(a1, qg[size_t(h) * kHeadDim + j1]);
+  }
+  qbar[size_t(g) * kHeadDim + j0] = a0;
+  qbar[size_t(g) * kHeadDim + j1] = a1;
+  // w = (qbar*qbar)*var as two rounded multiplies; -0 folded onto +0
+  const float w0 = __fadd_rn(__fmul_rn(__fmul_rn(a0, a0), var[size_t(g) * kHeadDim + j0]), 0.0f);
+  const float w1 = __fadd_rn(__fmul_rn(__fmul_rn(a1, a1), var[size_t(g) * kHeadDim + j1]), 0.0f);
+
+  constexpr int NT = UNIFORM ? 1 : 4;      // candidate bits per channel
+  const float step[4] = {1.0f, 0.25f, 0.0625f, 0.015625f};
+  uint32_t v0[NT], v1[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    v0[t] = __float_as_uint(__fmul_rn(w0, step[t]));
+    v1[t] = __float_as_uint(__fmul_rn(w1, step[t]));
+  }
+  const int total = NT * kHeadDim;
+  const int K = budget < total ? budget : total;
+
+  uint32_t T = 0;
+  if (K > 0) {
+    for (int bit = 30; bit >= 0; --bit) {
+      const uint32_t cand = T | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) cnt += wave_count(v0[t] >= cand) + wave_count(v1[t] >= cand);
+      if (cnt >= K) T = cand;
+    }
+  }
+  int gt = 0;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) gt += wave_count(v0[t] > T) + wave_count(v1[t] > T);
+  const int rem = K - gt;                  // bits to take among those equal to T
+
+  const uint64_t lt = (l == 0) ? 0ull : (~0ull >> (64 - l));
+  int before0 = 0, total0 = 0, before1 = 0;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const uint64_t e0 = __ballot(K > 0 && v0[t] == T);
+    before0 += __popcll(e0 & lt);
+    total0 += __popcll(e0);
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) before1 += __popcll(__ballot(K > 0 && v1[t] == T) & lt);
+  before1 += total0;
+
+  int d0 = 0, d1 = 0, r0 = before0, r1 = before1;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const bool eq0 = K > 0 && v0[t] == T, eq1 = K > 0 && v1[t] == T;
+    d0 += (K > 0 && v0[t] > T) || (eq0 && r0 < rem);
+    d1 += (K > 0 && v1[t] > T) || (eq1 && r1 < rem);
+    r0 += eq0;
+    r1 += eq1;
+  }
+  if (UNIFORM) {
+    d0 *= 4;
+    d1 *= 4;
+  }
+  depth[size_t(g) * kHeadDim + j0] = uint8_t(d0);
+  depth[size_t(g) * kHeadDim + j1] = uint8_t(d1);
+}
+
+}  // namespace sdq
+
+using namespace sdq;
+
+static int plan_common(const float* q, const float* key_var, int G, int H_grp, int d, int budget,
+                       uint8_t* depth, float* qbar, hipStream_t stream, bool uniform) {
+  const char* nm = uniform ? "fathom_plan_uniform" : "fathom_plan";
+  SDQ_REQUIRE(q && key_var && depth && qbar, "%s: null pointer", nm);
+  SDQ_REQUIRE(G >= 1 && H_grp >= 1, "%s: G=%d, H_grp=%d must be >= 1", nm, G, H_grp);
+  SDQ_REQUIRE(d == kHeadDim, "%s: d=%d unsupported (only 128)", nm, d);
+  SDQ_REQUIRE(budget >= 0, "%s: budget/channel count %d must be >= 0", nm, budget);
+  SDQ_REQUIRE(!uniform || budget <= d, "%s: n_channels=%d exceeds d=%d", nm, budget, d);
+  if (uniform)
+    hipLaunchKernelGGL(fathom_plan_kernel<true>, dim3(G), dim3(64), 0, stream, q, key_var, H_grp,
+                       budget, depth, qbar);
+  else
+    hipLaunchKernelGGL(fathom_plan_kernel<false>, dim3(G), dim3(64), 0, stream, q, key_var, H_grp,
+                       budget, depth, qbar);
+  return check_launch(nm);
+}
+
+extern "C" int fathom_plan(const float* q, const float* key_var, int G, int H_grp, int d,
+                           int budget_bits, uint8_t* depth, float* qbar, hipStream_t stream) {
+  return plan_common(q, key_var, G, H_grp, d, budget_bits, depth, qbar, stream, false);
+}
+
+extern "C" int fathom_plan_uniform(const float* q, const float* key_var, int G, int H_grp, int d,
+                                   int n_channels, uint8_t* depth, float* qbar,
+                                   hipStream_t stream) {
+  return plan_common(q, key_var, G, H_grp, d, n_channels, depth, qbar, stream, true);
+}

@@ -1,0 +1,262 @@
+"""ctypes binding of libsdq.so (declarations in include/sdq.h).
+
+Argument marshalling only: every function checks that the torch tensors it
+is handed live on the GPU, are contiguous and have the element size and
+shape the C entry point will assume, then passes raw device pointers and the
+current (or given) HIP stream.  All arithmetic runs in the library's HIP
+kernels; there is no fallback.  Output tensors may be passed in, otherwise
+they are allocated with torch.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsdq.so")
+
+SDQ_KEY_F32_MAX = 0
+SDQ_KEY_U8_MIN = 1
+D = 128
+
+_lib = None
+
+_c_int, _c_size, _vp, _f = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+_SIGS = {
+    "sdq_last_error": ([], ctypes.c_char_p),
+    "sdq_abi_version": ([], _c_int),
+    "fathom_ingest": ([_vp, _c_int, _c_int, _c_int, _vp, _vp, _vp], _c_int),
+    "minmax_summarize": ([_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp], _c_int),
+    "fathom_plan": ([_vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp], _c_int),
+    "fathom_plan_uniform": ([_vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp], _c_int),
+    "fathom_gather": ([_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp], _c_int),
+    "fathom_scan": ([_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp], _c_int),
+    "topk_select_workspace_bytes": ([_c_int, _c_int, _c_int, _c_int], _c_size),
+    "topk_select": ([_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _c_size, _vp], _c_int),
+    "hamming_scan": ([_vp, _vp, _c_int, _c_int, _vp, _vp], _c_int),
+    "minmax_block_scan": ([_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp], _c_int),
+    "gather_attend_workspace_bytes": ([_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int], _c_size),
+    "gather_attend": ([_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                       _c_int, _f, _vp, _vp, _c_size, _vp], _c_int),
+}
+
+
+class SDQError(RuntimeError):
+    pass
+
+
+def load(path: str = LIB_PATH):
+    """Load libsdq.so (torch's HIP runtime is loaded first and shared)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise SDQError(f"{path} is not built: run `python -m sparse_top_decode_query_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = lib
+    return _lib
+
+
+def exported_symbols():
+    return list(_SIGS)
+
+
+def _check(rc: int, name: str) -> None:
+    if rc != 0:
+        msg = load().sdq_last_error().decode(errors="replace")
+        raise SDQError(f"{name} failed ({rc}): {msg}")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return _vp(s.cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, elem: int, numel: int | None = None) -> _vp:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise SDQError(f"{name} must be a CUDA/HIP tensor")
+    if not t.is_contiguous():
+        raise SDQError(f"{name} must be contiguous")
+    if t.element_size() != elem:
+        raise SDQError(f"{name} must have {elem}-byte elements, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise SDQError(f"{name} has {t.numel()} elements, expected {numel}")
+    return _vp(t.data_ptr())
+
+
+def _out(t, shape, dtype, device, name, elem):
+    if t is None:
+        t = torch.empty(shape, dtype=dtype, device=device)
+    n = 1
+    for s in shape:
+        n *= s
+    _dev(t, name, elem, n)
+    return t
+
+
+# ------------------------------------------------------------------ ingest
+def fathom_ingest(keys, planes=None, meta=None, stream=None):
+    """keys bf16 [G][n][128] -> (planes uint32 [G][128][4][n/32], meta uint32 [G][128][n/64])."""
+    G, n, d = keys.shape
+    _dev(keys, "keys", 2)
+    planes = _out(planes, (G, d, 4, n // 32), torch.int32, keys.device, "planes", 4)
+    meta = _out(meta, (G, d, n // 64), torch.int32, keys.device, "meta", 4)
+    _check(load().fathom_ingest(_vp(keys.data_ptr()), G, n, d, _vp(planes.data_ptr()),
+                                _vp(meta.data_ptr()), _stream(stream)), "fathom_ingest")
+    return planes, meta
+
+
+def minmax_summarize(keys, block=16, bmin=None, bmax=None, stream=None):
+    """keys bf16 [RG][n][128] -> (bmin, bmax) fp16 bits [RG][n/block][128]."""
+    RG, n, d = keys.shape
+    _dev(keys, "keys", 2)
+    nb = n // block
+    bmin = _out(bmin, (RG, nb, d), torch.int16, keys.device, "bmin", 2)
+    bmax = _out(bmax, (RG, nb, d), torch.int16, keys.device, "bmax", 2)
+    _check(load().minmax_summarize(_vp(keys.data_ptr()), RG, n, d, block, _vp(bmin.data_ptr()),
+                                   _vp(bmax.data_ptr()), _stream(stream)), "minmax_summarize")
+    return bmin, bmax
+
+
+# ------------------------------------------------------------------ decode step
+def fathom_plan(q, key_var, budget_bits, depth=None, qbar=None, uniform_channels=None,
+                stream=None):
+    """q float32 [G*H_grp][128], key_var float32 [G][128] -> (depth uint8 [G][128], qbar float32 [G][128]).
+    With ``uniform_channels`` set, builds the uniform-depth baseline plan instead."""
+    G, d = key_var.shape
+    rows = q.shape[0]
+    if rows % G:
+        raise SDQError("q rows must be a multiple of G")
+    Hgrp = rows // G
+    _dev(q, "q", 4, rows * d)
+    _dev(key_var, "key_var", 4, G * d)
+    depth = _out(depth, (G, d), torch.uint8, q.device, "depth", 1)
+    qbar = _out(qbar, (G, d), torch.float32, q.device, "qbar", 4)
+    args = (_vp(q.data_ptr()), _vp(key_var.data_ptr()), G, Hgrp, d)
+    outs = (_vp(depth.data_ptr()), _vp(qbar.data_ptr()), _stream(stream))
+    if uniform_channels is None:
+        _check(load().fathom_plan(*args, int(budget_bits), *outs), "fathom_plan")
+    else:
+        _check(load().fathom_plan_uniform(*args, int(uniform_channels), *outs), "fathom_plan_uniform")
+    return depth, qbar
+
+
+def fathom_gather(planes_host, meta_host, depth, planes_dev, meta_dev, stream=None):
+    """Copy the plan's active plane prefixes from pinned host tensors to device tensors."""
+    G, d, four, nw = planes_host.shape
+    n = nw * 32
+    for t, nm in ((planes_host, "planes_host"), (meta_host, "meta_host")):
+        if t.is_cuda or not t.is_pinned() or not t.is_contiguous():
+            raise SDQError(f"{nm} must be a contiguous pinned host tensor")
+    if meta_host.numel() != G * d * (n // 64):
+        raise SDQError("meta_host has the wrong size")
+    _dev(depth, "depth", 1, G * d)
+    _dev(planes_dev, "planes_dev", 4, planes_host.numel())
+    _dev(meta_dev, "meta_dev", 4, meta_host.numel())
+    _check(load().fathom_gather(_vp(planes_host.data_ptr()), _vp(meta_host.data_ptr()),
+                                _vp(depth.data_ptr()), G, d, n, _vp(planes_dev.data_ptr()),
+                                _vp(meta_dev.data_ptr()), _stream(stream)), "fathom_gather")
+
+
+def fathom_scan(planes, meta, depth, qbar, n, scores=None, stream=None):
+    """-> scores float32 [G][n]."""
+    G, d = depth.shape
+    _dev(planes, "planes", 4, G * d * 4 * (n // 32))
+    _dev(meta, "meta", 4, G * d * (n // 64))
+    _dev(depth, "depth", 1, G * d)
+    _dev(qbar, "qbar", 4, G * d)
+    scores = _out(scores, (G, n), torch.float32, planes.device, "scores", 4)
+    _check(load().fathom_scan(_vp(planes.data_ptr()), _vp(meta.data_ptr()), _vp(depth.data_ptr()),
+                              _vp(qbar.data_ptr()), G, d, n, _vp(scores.data_ptr()), _stream(stream)),
+           "fathom_scan")
+    return scores
+
+
+def topk_workspace(rows, n, k, key_type, device="cuda"):
+    nbytes = int(load().topk_select_workspace_bytes(rows, n, k, key_type))
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def topk_select(keys, k, n_sink=0, n_local=0, idx=None, ws=None, stream=None):
+    """keys float32 (largest first) or uint8 (smallest first) [rows][n] ->
+    idx int32 [rows][k + n_sink + n_local], ascending, -1 padded."""
+    rows, n = keys.shape
+    if keys.dtype == torch.float32:
+        kt = SDQ_KEY_F32_MAX
+        _dev(keys, "keys", 4, rows * n)
+    elif keys.dtype == torch.uint8:
+        kt = SDQ_KEY_U8_MIN
+        _dev(keys, "keys", 1, rows * n)
+    else:
+        raise SDQError("keys must be float32 or uint8")
+    idx = _out(idx, (rows, k + n_sink + n_local), torch.int32, keys.device, "idx", 4)
+    need = int(load().topk_select_workspace_bytes(rows, n, k, kt))
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=keys.device)
+    _dev(ws, "ws", 1)
+    _check(load().topk_select(_vp(keys.data_ptr()), kt, rows, n, int(k), int(n_sink), int(n_local),
+                              _vp(idx.data_ptr()), _vp(ws.data_ptr()), ws.numel(), _stream(stream)),
+           "topk_select")
+    return idx
+
+
+def hamming_scan(sigs, qsig, dist=None, stream=None):
+    """sigs uint32 [H][n], qsig uint32 [H] -> dist uint8 [H][n]."""
+    H, n = sigs.shape
+    _dev(sigs, "sigs", 4, H * n)
+    _dev(qsig, "qsig", 4, H)
+    dist = _out(dist, (H, n), torch.uint8, sigs.device, "dist", 1)
+    _check(load().hamming_scan(_vp(sigs.data_ptr()), _vp(qsig.data_ptr()), H, n,
+                               _vp(dist.data_ptr()), _stream(stream)), "hamming_scan")
+    return dist
+
+
+def minmax_block_scan(bmin, bmax, q, scores=None, stream=None):
+    """bmin, bmax fp16 bits [RG][nb][128], q float32 [RG*H_grp][128] -> scores float32 [RG][nb]."""
+    RG, nb, d = bmin.shape
+    _dev(bmin, "bmin", 2, RG * nb * d)
+    _dev(bmax, "bmax", 2, RG * nb * d)
+    rows = q.numel() // d
+    if rows % RG:
+        raise SDQError("q rows must be a multiple of RG")
+    _dev(q, "q", 4, rows * d)
+    scores = _out(scores, (RG, nb), torch.float32, bmin.device, "scores", 4)
+    _check(load().minmax_block_scan(_vp(bmin.data_ptr()), _vp(bmax.data_ptr()), _vp(q.data_ptr()),
+                                    RG, rows // RG, nb, d, _vp(scores.data_ptr()), _stream(stream)),
+           "minmax_block_scan")
+    return scores
+
+
+def attend_workspace(R, Hq, Hkv, per_query_head, n_idx, block_tokens, device="cuda"):
+    nbytes = int(load().gather_attend_workspace_bytes(R, Hq, Hkv, int(per_query_head), n_idx,
+                                                      block_tokens, D))
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def gather_attend(q, K, V, idx, block_tokens=1, per_query_head=False, softmax_scale=None,
+                  out=None, ws=None, stream=None):
+    """q float32 [R][Hq][128]; K, V bf16 [R][Hkv][n][128]; idx int32 [R][Hsel][n_idx]
+    -> out float32 [R][Hq][128]."""
+    R, Hq, d = q.shape
+    _, Hkv, n, _ = K.shape
+    n_idx = idx.shape[-1]
+    Hsel = Hq if per_query_head else Hkv
+    _dev(q, "q", 4, R * Hq * d)
+    _dev(K, "K", 2, R * Hkv * n * d)
+    _dev(V, "V", 2, R * Hkv * n * d)
+    _dev(idx, "idx", 4, R * Hsel * n_idx)
+    out = _out(out, (R, Hq, d), torch.float32, q.device, "out", 4)
+    if ws is None:
+        ws = attend_workspace(R, Hq, Hkv, per_query_head, n_idx, block_tokens, q.device)
+    _dev(ws, "ws", 1)
+    scale = (1.0 / d ** 0.5) if softmax_scale is None else float(softmax_scale)
+    _check(load().gather_attend(_vp(q.data_ptr()), _vp(K.data_ptr()), _vp(V.data_ptr()),
+                                _vp(idx.data_ptr()), R, Hq, Hkv, int(bool(per_query_head)), n, n_idx,
+                                int(block_tokens), d, scale, _vp(out.data_ptr()), _vp(ws.data_ptr()),
+                                ws.numel(), _stream(stream)), "gather_attend")
+    return out

@@ -1,0 +1,64 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/sdq.h declares, and rejects invalid arguments with SDQ_EINVAL before
+launching anything (the calls below never reach a HIP API)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_top_decode_query_amd import lib as sdq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdq.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(sdq.LIB_PATH), reason="libsdq.so not built")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", src, re.M)
+    return sorted(set(names))
+
+
+def test_header_matches_binding():
+    assert _declared() == sorted(sdq.exported_symbols())
+
+
+def test_library_exports_every_declared_symbol():
+    L = sdq.load()
+    for name in _declared():
+        assert hasattr(L, name), name
+    assert L.sdq_abi_version() == 1
+
+
+def test_invalid_arguments_rejected_without_launch():
+    L = sdq.load()
+    p = ctypes.c_void_p(0x1000)       # never dereferenced: validation fails first
+    null = ctypes.c_void_p(0)
+    s = ctypes.c_void_p(0)
+    EINVAL = -1
+    assert L.fathom_scan(null, p, p, p, 8, 128, 4096, p, s) == EINVAL
+    assert b"null" in L.sdq_last_error()
+    assert L.fathom_scan(p, p, p, p, 8, 128, 4000, p, s) == EINVAL          # n % 64
+    assert L.fathom_scan(p, p, p, p, 8, 64, 4096, p, s) == EINVAL           # d != 128
+    assert L.fathom_plan(p, p, 8, 4, 128, -1, p, p, s) == EINVAL             # negative budget
+    assert L.fathom_plan_uniform(p, p, 8, 4, 128, 129, p, p, s) == EINVAL    # > d channels
+    assert L.fathom_ingest(p, 0, 4096, 128, p, p, s) == EINVAL               # G < 1
+    assert L.topk_select(p, 7, 1, 10, 2, 0, 0, p, p, 256, s) == EINVAL       # key type
+    assert L.topk_select(p, 0, 1, 10, 2, 6, 5, p, p, 256, s) == EINVAL       # windows > n
+    assert L.topk_select(p, 0, 8, 1 << 20, 512, 0, 0, p, null, 0, s) == EINVAL   # no workspace
+    assert L.hamming_scan(p, p, 0, 10, p, s) == EINVAL
+    assert L.minmax_block_scan(p, p, p, 1, 4, 0, 128, p, s) == EINVAL
+    assert L.gather_attend(p, p, p, p, 1, 32, 6, 0, 100, 8, 1, 128, 1.0, p, p, 1 << 20, s) == EINVAL
+    assert L.gather_attend(p, p, p, p, 1, 32, 8, 0, 100, 8, 1, 128, 1.0, p, p, 0, s) == EINVAL
+
+
+def test_workspace_sizes():
+    L = sdq.load()
+    assert L.topk_select_workspace_bytes(8, 1 << 20, 512, 0) >= 8 * 8192 * 8
+    assert L.topk_select_workspace_bytes(0, 10, 1, 0) == 0
+    ws = L.gather_attend_workspace_bytes(1, 32, 8, 0, 512, 1, 128)
+    assert ws == 32 * 8 * 130 * 4          # 8 chunks of 64 rows per query head
+    assert L.gather_attend_workspace_bytes(1, 32, 8, 0, 512, 1, 64) == 0
