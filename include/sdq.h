@@ -145,12 +145,17 @@ int fathom_gather(const uint32_t* planes_host, const uint32_t* meta_host, const 
  * where c is the t_j-bit code read from the first t_j planes and scale/offset
  * are that channel's 64-token block metadata (the midpoint of the t-bit bin,
  * the 4-bit dequantisation at t = 4).  Unread channels contribute nothing and
- * their metadata is not read.  Accumulation is float32.
+ * their metadata is not read; depths outside 1..4 count as unread.
+ * Accumulation is float32 (each channel's code times its weight is added with
+ * one fused multiply-add).
  *   planes, meta  as fathom_ingest;  depth, qbar as fathom_plan
  *   scores        float32 [G][n] out
+ *   block_max     float32 [G][n/64] out, or NULL: the maximum score of every
+ *                 64-token block (input of topk_select_block_max)
  * Errors: SDQ_EINVAL on null pointers, G < 1, n < 64, n % 64 != 0, d != 128. */
 int fathom_scan(const uint32_t* planes, const uint32_t* meta, const uint8_t* depth,
-                const float* qbar, int G, int d, int n, float* scores, hipStream_t stream);
+                const float* qbar, int G, int d, int n, float* scores, float* block_max,
+                hipStream_t stream);
 
 /* topk_select -- per-row top-k (HashAttention study notes, sec. 2.1 TOPK and
  * sec. 3.1 fixed positions; OasisKV review, per-KV-head top-K).
@@ -168,6 +173,18 @@ int fathom_scan(const uint32_t* planes, const uint32_t* meta, const uint8_t* dep
 size_t topk_select_workspace_bytes(int rows, int n, int k, int key_type);
 int topk_select(const void* keys, int key_type, int rows, int n, int k, int n_sink, int n_local,
                 int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* topk_select_block_max -- topk_select for float32 scores whose 64-key
+ * block maxima are already known (fathom_scan writes them).  Same ordering,
+ * windows and output as topk_select.  The k-th largest block maximum bounds
+ * the k-th largest score from below, so only the blocks whose maximum
+ * reaches it are read.  Needs no workspace.
+ *   keys       float32 [rows][n], 16-byte aligned
+ *   block_max  float32 [rows][n/64]: block_max[r][b] = max of keys[r][64b..64b+63]
+ * Errors: as topk_select, plus SDQ_EINVAL if block_max is null, if n, n_sink
+ * or n_local is not a multiple of 64, or n > 2^20. */
+int topk_select_block_max(const float* keys, const float* block_max, int rows, int n, int k,
+                          int n_sink, int n_local, int32_t* idx_out, hipStream_t stream);
 
 /* hamming_scan -- dist[h][i] = popcount(sigs[h][i] XOR qsig[h]) in [0, 32]
  * (HashAttention study notes, sec. 2.2).

@@ -12,6 +12,7 @@ namespace sdq {
 // One thread owns a pair of adjacent channels; the 64 threads of a wave cover
 // the 128 channels, so each token row (256 bytes) is read by one coalesced
 // 4-byte-per-lane load.  A workgroup walks `bpw` consecutive 64-token blocks.
+
 __global__ __launch_bounds__(64) void fathom_ingest_kernel(const uint32_t* __restrict__ keys,
                                                            int n, int nb64, int bpw,
                                                            uint32_t* __restrict__ planes,

@@ -5,130 +5,129 @@
 //   s_i = sum_{t_j>0} qbar_j * (off_bj + scale_bj * (c_ij * 2^(4-t_j) + (2^(4-t_j)-1)/2))
 // with c_ij the t_j-bit prefix code.  Since c * 2^(4-t) = sum_{p<t} bit_p * 2^(3-p),
 // every plane bit carries a weight that does not depend on t:
-//   s_i = C_b + sum_{p=0..3} 2^(3-p) * acc_p,  acc_p = sum_{j: t_j>p, bit_pij=1} qbar_j * scale_bj
+//   s_i = C_b + sum_{t_j>p} bit_pij * 2^(3-p) * w_bj,   w_bj = qbar_j * scale_bj
 //   C_b = sum_{t_j>0} qbar_j * off_bj + (qbar_j * (2^(4-t_j)-1)/2) * scale_bj
 //
-// Mapping onto a wave64: one wave owns a 64-token block at a time, lane l is
-// token 64b+l, so the 64-bit plane word of a block IS the set of lanes whose
-// bit is 1.  The word is fetched with a scalar load and used directly as a
-// lane mask (inverse ballot), and the block's fp16 scale, also a scalar load,
-// feeds a mixed-precision FMA (v_fma_mix_f32) without conversion.  C_b is
-// computed lane-parallel over (channel slot, block) pairs and reduced with
-// cross-lane shuffles.  The active channel list (sorted by depth) is built
-// once per workgroup in LDS.
+// Mapping onto CDNA: one lane owns one 32-token word of the planes, so every
+// plane row is read as 64 consecutive dwords per wave (256-byte coalesced
+// vector loads, each byte once), and the lane's 32 tokens share one 64-token
+// block, so the weights w_bj are per-lane values.  Tokens i and i+16 of the
+// word are handled together: two bit operations per plane move their t-bit
+// codes into the low and high 16-bit halves of one register, and a code
+// pattern c read as an fp16 is the denormal c * 2^-24 -- exact -- so one
+// v_fma_mix_f32 per token and channel adds c * (w_bj * 2^(24+4-t)) to a
+// float32 accumulator.  That is t+1 instructions per token and channel
+// instead of one extract and one multiply-add per bit.  The float32 constant
+// C_b is accumulated alongside.
+//
+// Loads in flight bound this kernel: each channel's metadata and plane words
+// come from a ring of buffers, three to six channels deep.
+//
+// Optionally the maximum score of every 64-token block is written as well
+// (the two lanes of a block combine theirs); top-k selection uses it to skip
+// blocks that cannot hold a winner.
 #include "common.hpp"
 
 namespace sdq {
 
 constexpr int kScanWaves = 4;
-constexpr int kScanTB = 8;     // 64-token blocks per wave tile
+constexpr int kTok = 32;                 // tokens per lane (one plane word)
 
-// The index is read-only for the whole launch: reading it through the
-// constant address space lets wave-uniform loads go to the scalar unit
-// (s_load into SGPRs) instead of vector loads plus v_readfirstlane.
-template <typename T>
-using cptr = const __attribute__((address_space(4))) T*;
-// The pointer is the same in every lane; readfirstlane makes that explicit
-// (the compiler cannot always prove it) so the address lives in SGPRs.
-template <typename T>
-__device__ __forceinline__ cptr<T> as_const(const T* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
-  return (cptr<T>)((uint64_t(hi) << 32) | lo);
-}
-
-struct ScanCtx {
-  const uint32_t* planes;
-  const uint32_t* meta;
-  size_t nw;          // 32-bit words per plane row (n/32)
-  int nb64;
-  int g;
-  int A;
-  const int* s_j;
-  const int* s_t;
-  const float* s_q;
-  const float* s_qm;
+template <int T>
+struct ChanData {
+  uint32_t mw;          // scale | offset << 16
+  uint32_t W[T];        // this lane's word of planes 0..T-1
 };
 
-template <int T, int TB>
-__device__ __forceinline__ void accum_channel(cptr<uint64_t> prow, size_t pstride,
-                                              cptr<uint32_t> mrow, float qv,
-                                              float (&acc)[4][TB]) {
+template <int T>
+__device__ __forceinline__ void load_chan(ChanData<T>& d, const uint32_t* mhead,
+                                          const uint32_t* phead, int j, int nb64, size_t nw) {
+  d.mw = mhead[size_t(j) * nb64];
+  const uint32_t* prow = phead + size_t(j) * 4 * nw;
 #pragma unroll
-  for (int k = 0; k < TB; ++k) {
-    const uint32_t mw = mrow[k];
-    const float sc = float(__builtin_bit_cast(_Float16, uint16_t(mw & 0xFFFFu)));
+  for (int p = 0; p < T; ++p) d.W[p] = prow[size_t(p) * nw];
+}
+
+// Adds one channel's contribution to the 32 scores of the lane's word.
+// q2 = qbar_j * 2^(28-t): with the fp16 scale it gives the weight of a t-bit
+// code read as an fp16 denormal (c * 2^-24).
+template <int T>
+__device__ __forceinline__ void use_chan(const ChanData<T>& d, float qv, float qm, float q2,
+                                         float& C, float (&acc)[kTok]) {
+  const float sc = half_bits_to_f32(d.mw);
+  const float off = half_bits_to_f32(d.mw >> 16);
+  C = __builtin_fmaf(off, qv, C);
+  C = __builtin_fmaf(sc, qm, C);
+  const float w = sc * q2;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    uint32_t x = 0;
 #pragma unroll
     for (int p = 0; p < T; ++p) {
-      const uint64_t m = prow[size_t(p) * pstride + k];
-      const float upd = __builtin_fmaf(sc, qv, acc[p][k]);
-      acc[p][k] = __builtin_amdgcn_inverse_ballot_w64(m) ? upd : acc[p][k];
+      const int sft = T - 1 - p;                // code bit of plane p
+      const uint32_t v = (i >= sft) ? (d.W[p] >> (i - sft)) : (d.W[p] << (sft - i));
+      x |= v & (0x00010001u << sft);           // tokens i (low half) and i+16 (high half)
     }
+    asm volatile("" : "+v"(x));                 // keep x whole: its halves feed op_sel
+    acc[i] = __builtin_fmaf(half_bits_to_f32(x), w, acc[i]);
+    acc[i + 16] = __builtin_fmaf(half_bits_to_f32(x >> 16), w, acc[i + 16]);
   }
 }
 
-template <int TB>
-__device__ __forceinline__ void scan_tile(const ScanCtx& c, int b0, float* __restrict__ out) {
-  const int lane = threadIdx.x & 63;
-  float acc[4][TB];
-#pragma unroll
-  for (int p = 0; p < 4; ++p)
-#pragma unroll
-    for (int k = 0; k < TB; ++k) acc[p][k] = 0.0f;
+// Loads in flight per lane are what bound this kernel (few waves, small
+// per-lane loads): a ring of D channel buffers keeps D-1 channels' plane words
+// and metadata in flight while one is accumulated.  The ring is indexed with
+// compile-time slots, so its registers never move.
+template <int T>
+struct RingDepth {
+  static constexpr int D = T == 1 ? 6 : (T == 2 ? 4 : 3);
+};
 
-  const size_t pstride = c.nw / 2;   // 64-bit words per plane row
-  for (int a = 0; a < c.A; ++a) {
-    const int j = __builtin_amdgcn_readfirstlane(c.s_j[a]);
-    const int t = __builtin_amdgcn_readfirstlane(c.s_t[a]);
-    const float qv = c.s_q[a];
-    const size_t row = size_t(c.g) * kHeadDim + j;
-    cptr<uint32_t> mrow = as_const(c.meta + row * c.nb64 + b0);
-    cptr<uint64_t> prow =
-        as_const(reinterpret_cast<const uint64_t*>(c.planes + row * 4 * c.nw) + b0);
-    switch (t) {
-      case 4: accum_channel<4, TB>(prow, pstride, mrow, qv, acc); break;
-      case 3: accum_channel<3, TB>(prow, pstride, mrow, qv, acc); break;
-      case 2: accum_channel<2, TB>(prow, pstride, mrow, qv, acc); break;
-      default: accum_channel<1, TB>(prow, pstride, mrow, qv, acc); break;
+// All channels of depth T: list slots [a, end).  Full turns of the ring are
+// straight-line code (D accumulations, each followed by the refill of its
+// slot), so the compiler keeps the refills where they are written and its
+// waits stay exact; refills past the end re-read the run's last channel (an
+// L1 hit).  The last partial turn only drains the ring.
+template <int T>
+__device__ __forceinline__ void accum_run(int a, int end, const int* s_j, const float* s_q,
+                                          const float* s_qm, const float* s_q2,
+                                          const uint32_t* mhead, const uint32_t* phead, int nb64,
+                                          size_t nw, float& C, float (&acc)[kTok]) {
+  constexpr int D = RingDepth<T>::D;
+  if (a >= end) return;
+  auto fetch = [&](ChanData<T>& d, int x) {
+    x = x < end ? x : end - 1;
+    load_chan<T>(d, mhead, phead, __builtin_amdgcn_readfirstlane(s_j[x]), nb64, nw);
+  };
+  ChanData<T> ring[D];
+#pragma unroll
+  for (int k = 0; k < D; ++k) fetch(ring[k], a + k);
+  const int turns = (end - a) / D;
+  for (int it = 0; it < turns; ++it) {
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+      use_chan<T>(ring[k], s_q[a + k], s_qm[a + k], s_q2[a + k], C, acc);
+      fetch(ring[k], a + k + D);
     }
+    a += D;
   }
-
-  // constant term per block, lane-parallel: lane = (channel slot, block)
-  constexpr int SLOTS = 64 / TB;
-  const int slot = lane / TB, kb = lane % TB;
-  float cacc = 0.0f;
-  for (int a0 = 0; a0 < c.A; a0 += SLOTS) {
-    const int a = a0 + slot;
-    if (a < c.A) {
-      const int j = c.s_j[a];
-      const uint32_t mw = c.meta[(size_t(c.g) * kHeadDim + j) * c.nb64 + b0 + kb];
-      const float off = float(__builtin_bit_cast(_Float16, uint16_t(mw >> 16)));
-      const float sc = float(__builtin_bit_cast(_Float16, uint16_t(mw & 0xFFFFu)));
-      cacc = __builtin_fmaf(off, c.s_q[a], cacc);
-      cacc = __builtin_fmaf(sc, c.s_qm[a], cacc);
-    }
-  }
+  const int rem = end - a;
 #pragma unroll
-  for (int m = TB; m < 64; m <<= 1) cacc += __shfl_xor(cacc, m, 64);
-
-#pragma unroll
-  for (int k = 0; k < TB; ++k) {
-    const float ck = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cacc), k));
-    const float s = ((acc[0][k] * 8.0f + acc[1][k] * 4.0f) + acc[2][k] * 2.0f) + acc[3][k];
-    out[size_t(b0 + k) * 64 + lane] = s + ck;
-  }
+  for (int k = 0; k < D; ++k)
+    if (k < rem) use_chan<T>(ring[k], s_q[a + k], s_qm[a + k], s_q2[a + k], C, acc);
 }
 
 __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
     const uint32_t* __restrict__ planes, const uint32_t* __restrict__ meta,
     const uint8_t* __restrict__ depth, const float* __restrict__ qbar, int n, int nb64,
-    float* __restrict__ scores) {
+    float* __restrict__ scores, float* __restrict__ block_max) {
+  __shared__ float s_q2[kHeadDim];
   __shared__ int s_j[kHeadDim];
   __shared__ int s_t[kHeadDim];
   __shared__ float s_q[kHeadDim];
   __shared__ float s_qm[kHeadDim];
   __shared__ int s_A;
+  __shared__ int s_run[5];          // list slots where depth 4, 3, 2, 1 start; s_run[4] = A
   const int g = blockIdx.y;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -140,6 +139,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     int base = 0;
     for (int L = 4; L >= 1; --L) {
+      if (lane == 0) s_run[4 - L] = base;
       const uint64_t b0 = __ballot(t0 == L), b1 = __ballot(t1 == L);
       if (t0 == L) {
         const int pos = base + __popcll(b0 & lt);
@@ -153,7 +153,10 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
       }
       base += __popcll(b0) + __popcll(b1);
     }
-    if (lane == 0) s_A = base;
+    if (lane == 0) {
+      s_A = base;
+      s_run[4] = base;
+    }
   }
   __syncthreads();
   const int A = __builtin_amdgcn_readfirstlane(s_A);
@@ -163,18 +166,48 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
     const float half_gap = float((1 << (4 - s_t[tid])) - 1) * 0.5f;
     s_q[tid] = qv;
     s_qm[tid] = qv * half_gap;
+    s_q2[tid] = qv * float(1u << (28 - s_t[tid]));
   }
   __syncthreads();
 
-  ScanCtx c{planes, meta, size_t(n) / 32, nb64, g, A, s_j, s_t, s_q, s_qm};
-  float* out = scores + size_t(g) * n;
-  // wave index is uniform within a wave; say so, so that tile addresses stay scalar
-  const int b0 = __builtin_amdgcn_readfirstlane((blockIdx.x * kScanWaves + wave) * kScanTB);
-  if (b0 >= nb64) return;
-  if (b0 + kScanTB <= nb64) {
-    scan_tile<kScanTB>(c, b0, out);
-  } else {
-    for (int b = b0; b < nb64; ++b) scan_tile<1>(c, b, out);
+  const size_t nw = size_t(n) / 32;
+  const int wd = (blockIdx.x * kScanWaves + wave) * 64 + lane;   // this lane's 32-token word
+  if ((blockIdx.x * kScanWaves + wave) * 64 >= int(nw)) return;   // whole wave past the end
+  const bool valid = wd < int(nw);
+  const int wdc = valid ? wd : int(nw) - 1;                       // loads stay in bounds
+  const int b = wdc >> 1;
+  const uint32_t* mhead = meta + size_t(g) * kHeadDim * nb64 + b;
+  const uint32_t* phead = planes + size_t(g) * kHeadDim * 4 * nw + wdc;
+
+  // Channels are sorted by depth, so four fixed-depth runs cover them and the
+  // accumulators never change registers.
+  float C = 0.0f;
+  float acc[kTok];
+#pragma unroll
+  for (int i = 0; i < kTok; ++i) acc[i] = 0.0f;
+  const int r0 = __builtin_amdgcn_readfirstlane(s_run[0]), r1 = __builtin_amdgcn_readfirstlane(s_run[1]);
+  const int r2 = __builtin_amdgcn_readfirstlane(s_run[2]), r3 = __builtin_amdgcn_readfirstlane(s_run[3]);
+  accum_run<4>(r0, r1, s_j, s_q, s_qm, s_q2, mhead, phead, nb64, nw, C, acc);
+  accum_run<3>(r1, r2, s_j, s_q, s_qm, s_q2, mhead, phead, nb64, nw, C, acc);
+  accum_run<2>(r2, r3, s_j, s_q, s_qm, s_q2, mhead, phead, nb64, nw, C, acc);
+  accum_run<1>(r3, A, s_j, s_q, s_qm, s_q2, mhead, phead, nb64, nw, C, acc);
+
+  float sv[kTok];
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kTok; ++i) {
+    sv[i] = acc[i] + C;
+    m = fmaxf(m, sv[i]);
+  }
+  if (valid) {
+    float4* dst = reinterpret_cast<float4*>(scores + size_t(g) * n + size_t(wd) * kTok);
+#pragma unroll
+    for (int v = 0; v < kTok / 4; ++v)
+      dst[v] = make_float4(sv[4 * v], sv[4 * v + 1], sv[4 * v + 2], sv[4 * v + 3]);
+  }
+  if (block_max) {
+    m = fmaxf(m, __shfl_xor(m, 1, 64));
+    if (valid && (lane & 1) == 0) block_max[size_t(g) * nb64 + b] = m;
   }
 }
 
@@ -183,15 +216,17 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
 using namespace sdq;
 
 extern "C" int fathom_scan(const uint32_t* planes, const uint32_t* meta, const uint8_t* depth,
-                           const float* qbar, int G, int d, int n, float* scores,
+                           const float* qbar, int G, int d, int n, float* scores, float* block_max,
                            hipStream_t stream) {
   SDQ_REQUIRE(planes && meta && depth && qbar && scores, "fathom_scan: null pointer");
   SDQ_REQUIRE(G >= 1, "fathom_scan: G=%d must be >= 1", G);
   SDQ_REQUIRE(n >= 64 && n % 64 == 0, "fathom_scan: n=%d must be a positive multiple of 64", n);
   SDQ_REQUIRE(d == kHeadDim, "fathom_scan: d=%d unsupported (only 128)", d);
+  SDQ_REQUIRE(reinterpret_cast<uintptr_t>(scores) % 16 == 0, "fathom_scan: scores must be 16-byte aligned");
   const int nb64 = n / 64;
-  dim3 grid(cdiv(nb64, kScanWaves * kScanTB), G);
+  const size_t nw = size_t(n) / 32;
+  dim3 grid(cdiv(nw, kScanWaves * 64), G);
   hipLaunchKernelGGL(fathom_scan_kernel, grid, dim3(kScanWaves * 64), 0, stream, planes, meta,
-                     depth, qbar, n, nb64, scores);
+                     depth, qbar, n, nb64, scores, block_max);
   return check_launch("fathom_scan");
 }

@@ -85,6 +85,103 @@ __device__ __forceinline__ void block_scan2(int a, int b, int& ea, int& eb, int&
   __syncthreads();
 }
 
+// k-th largest of a set of 32-bit codes, for a whole 512-thread workgroup.
+// fetch(i, &u) returns false for items that do not take part.  Each pass
+// histograms the codes inside the current range [lo, hi] into 256 bins of
+// width 2^s chosen so the bins span the range (bins follow the data, so
+// clustered codes do not pile onto one LDS counter), then narrows the range
+// to the bin holding the k-th code.  Returns the code T and how many of the
+// codes equal to T belong to the top k (`need`).
+struct KthResult {
+  uint32_t T;
+  int need;
+};
+
+template <typename Fetch>
+__device__ KthResult select_kth(int count, int K, Fetch fetch, uint32_t* hist, uint32_t* s_red) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // range of the codes
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  for (int i = tid; i < count; i += kTkThreads) {
+    uint32_t u;
+    if (fetch(i, &u)) {
+      mn = u < mn ? u : mn;
+      mx = u > mx ? u : mx;
+    }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const uint32_t a = __shfl_xor(mn, m, 64), b = __shfl_xor(mx, m, 64);
+    mn = a < mn ? a : mn;
+    mx = b > mx ? b : mx;
+  }
+  if (lane == 0) {
+    s_red[wave] = mn;
+    s_red[kTkWaves + wave] = mx;
+  }
+  __syncthreads();
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int w = 0; w < kTkWaves; ++w) {
+    lo = s_red[w] < lo ? s_red[w] : lo;
+    hi = s_red[kTkWaves + w] > hi ? s_red[kTkWaves + w] : hi;
+  }
+  __syncthreads();
+  int need = K;
+  while (lo < hi) {
+    const uint32_t width = hi - lo;
+    const int bits = 32 - __clz(width);                 // width < 2^bits
+    const int sh = bits > 8 ? bits - 8 : 0;              // (width >> sh) < 256
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < count; i += kTkThreads) {
+      uint32_t u;
+      if (fetch(i, &u) && u >= lo && u <= hi) atomicAdd(&hist[(u - lo) >> sh], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      const int l = tid;
+      const int c0 = hist[4 * l], c1 = hist[4 * l + 1], c2 = hist[4 * l + 2], c3 = hist[4 * l + 3];
+      const int lsum = c0 + c1 + c2 + c3;
+      int sfx = lsum;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_down(sfx, off, 64);
+        if (l + off < 64) sfx += y;
+      }
+      const int above = sfx - lsum;
+      const int S3 = above + c3, S2 = S3 + c2, S1 = S2 + c1, S0 = S1 + c0;
+      if (S3 >= need && above < need) { s_red[0] = 4 * l + 3; s_red[1] = need - above; }
+      if (S2 >= need && S3 < need) { s_red[0] = 4 * l + 2; s_red[1] = need - S3; }
+      if (S1 >= need && S2 < need) { s_red[0] = 4 * l + 1; s_red[1] = need - S2; }
+      if (S0 >= need && S1 < need) { s_red[0] = 4 * l; s_red[1] = need - S1; }
+    }
+    __syncthreads();
+    const uint32_t d = s_red[0];
+    need = int(s_red[1]);
+    __syncthreads();
+    const uint32_t nlo = lo + (d << sh);
+    const uint32_t span = (sh >= 32) ? 0xFFFFFFFFu : ((1u << sh) - 1u);
+    hi = (hi - nlo) > span ? nlo + span : hi;
+    lo = nlo;
+  }
+  return KthResult{lo, need};
+}
+
+// Reserves one slot per lane with pred set, one LDS atomic per wave.  The
+// slots of a wave are consecutive in lane order.
+__device__ __forceinline__ int wave_append(bool pred, int* counter) {
+  const uint64_t mask = __ballot(pred);
+  if (!mask) return -1;
+  const int lane = threadIdx.x & 63;
+  const int leader = __ffsll((unsigned long long)mask) - 1;
+  int base = 0;
+  if (lane == leader) base = atomicAdd(counter, __popcll(mask));
+  base = __shfl(base, leader, 64);
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  return pred ? base + __popcll(mask & lt) : -1;
+}
+
 // Writes the fixed positions and padding of one output row.
 __device__ __forceinline__ void write_fixed(int32_t* o, int n, int n_sink, int n_local, int K,
                                             int stride) {
@@ -99,8 +196,6 @@ template <int KT>
 __device__ void topk_row(const void* __restrict__ keys, size_t base, int n, int k, int n_sink,
                          int n_local, int32_t* __restrict__ o, int stride) {
   __shared__ uint32_t hist[256];
-  __shared__ uint32_t sh_digit;
-  __shared__ int sh_need;
   __shared__ int s_scan[2 * kTkWaves];
   const int tid = threadIdx.x;
   const int lo = n_sink, hi = n - n_local, m = hi - lo;
@@ -112,42 +207,16 @@ __device__ void topk_row(const void* __restrict__ keys, size_t base, int n, int 
   }
   if (K == 0) return;
 
-  uint32_t prefix = 0, pmask = 0;
-  int need = K;
-  const int first_shift = (KT == SDQ_KEY_U8_MIN) ? 0 : 24;
-  for (int shift = first_shift; shift >= 0; shift -= 8) {
-    if (tid < 256) hist[tid] = 0;
-    __syncthreads();
-    for (int i = lo + tid; i < hi; i += kTkThreads) {
-      const uint32_t u = load_code<KT>(keys, base + i);
-      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (tid < 64) {
-      // suffix sums over the 256 bins; lane l owns bins 4l..4l+3
-      const int l = tid;
-      const int c0 = hist[4 * l], c1 = hist[4 * l + 1], c2 = hist[4 * l + 2], c3 = hist[4 * l + 3];
-      const int lsum = c0 + c1 + c2 + c3;
-      int sfx = lsum;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_down(sfx, off, 64);
-        if (l + off < 64) sfx += y;
-      }
-      const int above = sfx - lsum;               // codes in higher lanes' bins
-      const int S3 = above + c3, S2 = S3 + c2, S1 = S2 + c1, S0 = S1 + c0;
-      if (S3 >= need && above < need) { sh_digit = 4 * l + 3; sh_need = need - above; }
-      if (S2 >= need && S3 < need) { sh_digit = 4 * l + 2; sh_need = need - S3; }
-      if (S1 >= need && S2 < need) { sh_digit = 4 * l + 1; sh_need = need - S2; }
-      if (S0 >= need && S1 < need) { sh_digit = 4 * l; sh_need = need - S1; }
-    }
-    __syncthreads();
-    prefix |= sh_digit << shift;
-    pmask |= 255u << shift;
-    need = sh_need;
-    __syncthreads();
-  }
-  const uint32_t T = prefix;       // k-th largest code; keep every u > T and the first `need` u == T
+  __shared__ uint32_t s_red[2 * kTkWaves];
+  const KthResult kr = select_kth(
+      m, K,
+      [&](int i, uint32_t* u) {
+        *u = load_code<KT>(keys, base + lo + i);
+        return true;
+      },
+      hist, s_red);
+  const uint32_t T = kr.T;         // k-th largest code; keep every u > T and the first `need` u == T
+  const int need = kr.need;
 
   constexpr int IPT = 8;
   int out_pos = n_sink, eq_seen = 0;
@@ -306,8 +375,6 @@ __global__ __launch_bounds__(kTkThreads) void topk_final_kernel(const float* __r
                                                                 int stride) {
   __shared__ uint64_t ck[kCandCap];       // composite keys (u << 32) | ~index
   __shared__ uint32_t hist[256];
-  __shared__ uint32_t sh_digit;
-  __shared__ int sh_need;
   __shared__ int sh_cnt;
   const int row = blockIdx.x, tid = threadIdx.x;
   int32_t* o = out + size_t(row) * stride;
@@ -326,40 +393,23 @@ __global__ __launch_bounds__(kTkThreads) void topk_final_kernel(const float* __r
     ck[i] = (uint64_t(c.x) << 32) | uint64_t(~c.y);
   }
   __syncthreads();
-  // radix select of the K-th largest composite key (all distinct)
-  uint64_t prefix = 0, pmask = 0;
-  int need = K;
-  for (int shift = 56; shift >= 0; shift -= 8) {
-    if (tid < 256) hist[tid] = 0;
-    __syncthreads();
-    for (int i = tid; i < cnt; i += kTkThreads) {
-      const uint64_t v = ck[i];
-      if ((v & pmask) == prefix) atomicAdd(&hist[uint32_t(v >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (tid < 64) {
-      const int l = tid;
-      const int c0 = hist[4 * l], c1 = hist[4 * l + 1], c2 = hist[4 * l + 2], c3 = hist[4 * l + 3];
-      const int lsum = c0 + c1 + c2 + c3;
-      int sfx = lsum;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_down(sfx, off, 64);
-        if (l + off < 64) sfx += y;
-      }
-      const int above = sfx - lsum;
-      const int S3 = above + c3, S2 = S3 + c2, S1 = S2 + c1, S0 = S1 + c0;
-      if (S3 >= need && above < need) { sh_digit = 4 * l + 3; sh_need = need - above; }
-      if (S2 >= need && S3 < need) { sh_digit = 4 * l + 2; sh_need = need - S3; }
-      if (S1 >= need && S2 < need) { sh_digit = 4 * l + 1; sh_need = need - S2; }
-      if (S0 >= need && S1 < need) { sh_digit = 4 * l; sh_need = need - S1; }
-    }
-    __syncthreads();
-    prefix |= uint64_t(sh_digit) << shift;
-    pmask |= uint64_t(255) << shift;
-    need = sh_need;
-    __syncthreads();
-  }
+  __shared__ uint32_t s_red[2 * kTkWaves];
+  const KthResult k2 = select_kth(
+      cnt, K,
+      [&](int i, uint32_t* u) {
+        *u = uint32_t(ck[i] >> 32);
+        return true;
+      },
+      hist, s_red);
+  const KthResult k3 = select_kth(
+      cnt, k2.need,
+      [&](int i, uint32_t* u) {
+        const uint64_t v = ck[i];
+        *u = uint32_t(v);
+        return uint32_t(v >> 32) == k2.T;
+      },
+      hist, s_red);
+  const uint64_t prefix = (uint64_t(k2.T) << 32) | k3.T;   // exactly K composites are >= it
   // winners: composite >= prefix (exactly K of them); gather their indices
   __shared__ int widx[kCandCap];
   if (tid == 0) sh_cnt = 0;
@@ -392,6 +442,177 @@ __global__ __launch_bounds__(kTkThreads) void topk_final_kernel(const float* __r
   for (int i = tid; i < K; i += kTkThreads) o[n_sink + i] = widx[i];
 }
 
+
+// ------------------------------------------------------------- block-max path
+// Rows whose competition range is made of whole 64-key blocks.  With M_b the
+// maximum of block b, the k-th largest block maximum T satisfies T <= the
+// k-th largest key (the k blocks whose maxima are >= T hold k keys >= T), so
+// every key of the exact top-k lies in a block with M_b >= T and is >= T
+// itself.  One workgroup per row: select T among the block maxima in LDS,
+// read only the candidate blocks, keep their keys >= T, then select exactly
+// among those (composite key (u, ~index)) and sort the winners by index.
+// Rows where the candidates overflow fall back to the row path.
+constexpr int kBmMaxBlocks = 16384;     // block maxima held in LDS (n <= 2^20)
+constexpr int kBmCandBlocks = 2048;     // candidate blocks read
+constexpr int kBmCap = 4096;            // candidate keys
+
+__global__ __launch_bounds__(256) void topk_block_max_kernel(const float* __restrict__ keys, int n,
+                                                             int nb, float* __restrict__ bm) {
+  const int row = blockIdx.y;
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (b >= nb) return;
+  float v = keys[size_t(row) * n + size_t(b) * 64 + (threadIdx.x & 63)];
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  if ((threadIdx.x & 63) == 0) bm[size_t(row) * nb + b] = v;
+}
+
+__global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __restrict__ keys,
+                                                             const float* __restrict__ bm, int n,
+                                                             int nb, int k, int n_sink, int n_local,
+                                                             int32_t* __restrict__ out, int stride) {
+  __shared__ uint32_t bmc[kBmMaxBlocks];      // block-max codes; reused for the winners' indices
+  __shared__ int cb[kBmCandBlocks];
+  __shared__ uint64_t cand[kBmCap];
+  __shared__ uint32_t hist[256];
+  __shared__ int sh_ncb, sh_ncand;
+  const int row = blockIdx.x, tid = threadIdx.x;
+  int32_t* o = out + size_t(row) * stride;
+  const int lo = n_sink, hi = n - n_local, m = hi - lo;
+  const int blo = lo / 64, nbc = m / 64;        // competition blocks [blo, blo + nbc)
+  const int K = k < m ? k : m;
+  const size_t base = size_t(row) * n;
+  if (K == m || K == 0 || K > nbc || K > kBmCap) {
+    topk_row<SDQ_KEY_F32_MAX>(keys, base, n, k, n_sink, n_local, o, stride);
+    return;
+  }
+  // 1. block-max codes (8 loads in flight per thread)
+  for (int b0 = 0; b0 < nbc; b0 += 8 * kTkThreads) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int b = b0 + u * kTkThreads + tid;
+      v[u] = b < nbc ? bm[size_t(row) * nb + blo + b] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int b = b0 + u * kTkThreads + tid;
+      if (b < nbc) bmc[b] = f32_order_key(v[u]);
+    }
+  }
+  if (tid == 0) {
+    sh_ncb = 0;
+    sh_ncand = 0;
+  }
+  __syncthreads();
+  // 2. K-th largest block-max code
+  __shared__ uint32_t s_red[2 * kTkWaves];
+  const uint32_t T = select_kth(
+                         nbc, K,
+                         [&](int i, uint32_t* u) {
+                           *u = bmc[i];
+                           return true;
+                         },
+                         hist, s_red)
+                         .T;
+  // 3. candidate blocks
+  for (int b0 = 0; b0 < nbc; b0 += kTkThreads) {
+    const int b = b0 + tid;
+    const int slot = wave_append(b < nbc && bmc[b] >= T, &sh_ncb);
+    if (slot >= 0 && slot < kBmCandBlocks) cb[slot] = blo + b;
+  }
+  __syncthreads();
+  const int ncb = sh_ncb;
+  if (ncb > kBmCandBlocks) {
+    topk_row<SDQ_KEY_F32_MAX>(keys, base, n, k, n_sink, n_local, o, stride);
+    return;
+  }
+  // 4. candidate keys: (block, 16-byte part) items, four loads in flight per
+  // thread before any is used
+  const int items = ncb * 16;
+  for (int it0 = 0; it0 < items; it0 += 4 * kTkThreads) {
+    float4 v[4];
+    int e0[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int it = it0 + u * kTkThreads + tid;
+      e0[u] = it < items ? cb[it >> 4] * 64 + (it & 15) * 4 : -1;
+      v[u] = e0[u] >= 0 ? *reinterpret_cast<const float4*>(keys + base + e0[u])
+                        : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float vv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t uc = e0[u] >= 0 ? f32_order_key(vv[e]) : 0u;
+        const int slot = wave_append(e0[u] >= 0 && uc >= T, &sh_ncand);
+        if (slot >= 0 && slot < kBmCap) cand[slot] = (uint64_t(uc) << 32) | uint64_t(~uint32_t(e0[u] + e));
+      }
+    }
+  }
+  __syncthreads();
+  const int nc = sh_ncand;
+  if (nc > kBmCap) {
+    topk_row<SDQ_KEY_F32_MAX>(keys, base, n, k, n_sink, n_local, o, stride);
+    return;
+  }
+  // 5. exact selection among the candidates: the K-th largest code T2 and
+  // how many codes equal to T2 to keep, then among those the lowest indices
+  const KthResult k2 = select_kth(
+      nc, K,
+      [&](int i, uint32_t* u) {
+        *u = uint32_t(cand[i] >> 32);
+        return true;
+      },
+      hist, s_red);
+  uint32_t idx_cut = 0;            // largest ~index kept among codes equal to T2
+  {
+    const KthResult k3 = select_kth(
+        nc, k2.need,
+        [&](int i, uint32_t* u) {
+          const uint64_t v = cand[i];
+          *u = uint32_t(v);
+          return uint32_t(v >> 32) == k2.T;
+        },
+        hist, s_red);
+    idx_cut = k3.T;
+  }
+  const uint64_t pre = (uint64_t(k2.T) << 32) | idx_cut;   // exactly K composites are >= pre
+  // 6. winners sorted by index (bitonic over the next power of two)
+  int* widx = reinterpret_cast<int*>(bmc);
+  if (tid == 0) sh_ncb = 0;
+  __syncthreads();
+  for (int i0 = 0; i0 < nc; i0 += kTkThreads) {
+    const int i = i0 + tid;
+    const bool win = i < nc && cand[i] >= pre;
+    const int slot = wave_append(win, &sh_ncb);
+    if (slot >= 0 && slot < kBmCap) widx[slot] = int(~uint32_t(cand[i]));
+  }
+  int P = 1;
+  while (P < K) P <<= 1;
+  __syncthreads();
+  for (int i = K + tid; i < P; i += kTkThreads) widx[i] = 0x7FFFFFFF;
+  __syncthreads();
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int st = size >> 1; st > 0; st >>= 1) {
+      for (int t = tid; t < P / 2; t += kTkThreads) {
+        const int i = 2 * t - (t & (st - 1));
+        const int j = i + st;
+        const bool up = (i & size) == 0;
+        const int a = widx[i], b = widx[j];
+        if ((a > b) == up) {
+          widx[i] = b;
+          widx[j] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  write_fixed(o, n, n_sink, n_local, K, stride);
+  for (int i = tid; i < K; i += kTkThreads) o[n_sink + i] = widx[i];
+}
+
 }  // namespace sdq
 
 using namespace sdq;
@@ -401,38 +622,74 @@ static bool use_fast(int n, int n_sink, int n_local, int k, int key_type) {
   return key_type == SDQ_KEY_F32_MAX && m >= kFastMinComp && k < m && k <= kCandCap;
 }
 
+static bool use_block_max(int n, int n_sink, int n_local, int k, int key_type) {
+  const int m = n - n_sink - n_local;
+  return key_type == SDQ_KEY_F32_MAX && m >= kFastMinComp && n % 64 == 0 && n_sink % 64 == 0 &&
+         n_local % 64 == 0 && n / 64 <= kBmMaxBlocks && k < m && k <= kBmCap && k <= m / 64;
+}
+
 extern "C" size_t topk_select_workspace_bytes(int rows, int n, int k, int key_type) {
   if (rows < 1 || n < 1) return 0;
   (void)k;
-  if (key_type == SDQ_KEY_F32_MAX && n >= kFastMinComp) return size_t(rows) * fast_ws_per_row();
+  if (key_type == SDQ_KEY_F32_MAX && n >= kFastMinComp) {
+    const size_t hist = size_t(rows) * fast_ws_per_row();
+    const size_t bm = size_t(rows) * size_t((n + 63) / 64) * sizeof(float);
+    return hist > bm ? hist : bm;
+  }
   return 256;
+}
+
+static int topk_validate(const char* nm, const void* keys, int key_type, int rows, int n, int k,
+                         int n_sink, int n_local, const int32_t* idx_out, int* stride) {
+  SDQ_REQUIRE(keys && idx_out, "%s: null pointer", nm);
+  SDQ_REQUIRE(key_type == SDQ_KEY_F32_MAX || key_type == SDQ_KEY_U8_MIN,
+              "%s: unknown key_type %d", nm, key_type);
+  SDQ_REQUIRE(rows >= 1 && n >= 1, "%s: rows=%d, n=%d must be >= 1", nm, rows, n);
+  SDQ_REQUIRE(k >= 0 && n_sink >= 0 && n_local >= 0, "%s: k, n_sink, n_local must be >= 0", nm);
+  SDQ_REQUIRE(n_sink <= n - n_local, "%s: n_sink + n_local = %d exceeds n = %d", nm,
+              n_sink + n_local, n);
+  const long long stride_ll = (long long)k + n_sink + n_local;
+  SDQ_REQUIRE(stride_ll <= 0x7FFFFFFF, "%s: output row too long", nm);
+  *stride = int(stride_ll);
+  return SDQ_OK;
+}
+
+static void launch_block_max_select(const float* fk, const float* bm, int rows, int n, int k,
+                                    int n_sink, int n_local, int32_t* idx_out, int stride,
+                                    hipStream_t stream) {
+  hipLaunchKernelGGL(topk_bm_kernel, dim3(rows), dim3(kTkThreads), 0, stream, fk, bm, n, n / 64, k,
+                     n_sink, n_local, idx_out, stride);
 }
 
 extern "C" int topk_select(const void* keys, int key_type, int rows, int n, int k, int n_sink,
                            int n_local, int32_t* idx_out, void* ws, size_t ws_bytes,
                            hipStream_t stream) {
-  SDQ_REQUIRE(keys && idx_out, "topk_select: null pointer");
-  SDQ_REQUIRE(key_type == SDQ_KEY_F32_MAX || key_type == SDQ_KEY_U8_MIN,
-              "topk_select: unknown key_type %d", key_type);
-  SDQ_REQUIRE(rows >= 1 && n >= 1, "topk_select: rows=%d, n=%d must be >= 1", rows, n);
-  SDQ_REQUIRE(k >= 0 && n_sink >= 0 && n_local >= 0, "topk_select: k, n_sink, n_local must be >= 0");
-  SDQ_REQUIRE(n_sink <= n - n_local, "topk_select: n_sink + n_local = %d exceeds n = %d",
-              n_sink + n_local, n);
-  const long long stride_ll = (long long)k + n_sink + n_local;
-  SDQ_REQUIRE(stride_ll <= 0x7FFFFFFF, "topk_select: output row too long");
-  const int stride = int(stride_ll);
-  const size_t need_ws = topk_select_workspace_bytes(rows, n, k, key_type);
+  int stride = 0;
+  const int rc = topk_validate("topk_select", keys, key_type, rows, n, k, n_sink, n_local, idx_out,
+                               &stride);
+  if (rc != SDQ_OK) return rc;
   if (stride == 0) return SDQ_OK;
+  const size_t need_ws = topk_select_workspace_bytes(rows, n, k, key_type);
+  const float* fk = reinterpret_cast<const float*>(keys);
+  if (use_block_max(n, n_sink, n_local, k, key_type) &&
+      reinterpret_cast<uintptr_t>(keys) % 16 == 0) {
+    SDQ_REQUIRE(ws && ws_bytes >= need_ws, "topk_select: workspace of %zu bytes needed, %zu given",
+                need_ws, ws_bytes);
+    float* bm = reinterpret_cast<float*>(ws);
+    const int nb = n / 64;
+    hipLaunchKernelGGL(topk_block_max_kernel, dim3(cdiv(nb, 4), rows), dim3(256), 0, stream, fk, n,
+                       nb, bm);
+    launch_block_max_select(fk, bm, rows, n, k, n_sink, n_local, idx_out, stride, stream);
+    return check_launch("topk_select");
+  }
   if (use_fast(n, n_sink, n_local, k, key_type)) {
     SDQ_REQUIRE(ws && ws_bytes >= need_ws, "topk_select: workspace of %zu bytes needed, %zu given",
                 need_ws, ws_bytes);
     const int lo = n_sink, hi = n - n_local;
-    const float* fk = reinterpret_cast<const float*>(keys);
     dim3 g2(cdiv(hi - lo, kFastChunk), rows);
     hipLaunchKernelGGL(topk_clear_kernel, dim3(rows), dim3(256), 0, stream, ws);
     hipLaunchKernelGGL(topk_hist_kernel, g2, dim3(256), 0, stream, fk, n, lo, hi, ws);
-    const int K = k;
-    hipLaunchKernelGGL(topk_bin_kernel, dim3(rows), dim3(256), 0, stream, ws, K);
+    hipLaunchKernelGGL(topk_bin_kernel, dim3(rows), dim3(256), 0, stream, ws, k);
     hipLaunchKernelGGL(topk_collect_kernel, g2, dim3(256), 0, stream, fk, n, lo, hi, ws);
     hipLaunchKernelGGL(topk_final_kernel, dim3(rows), dim3(kTkThreads), 0, stream, fk, n, k, n_sink,
                        n_local, ws, idx_out, stride);
@@ -445,4 +702,21 @@ extern "C" int topk_select(const void* keys, int key_type, int rows, int n, int 
     hipLaunchKernelGGL(topk_row_kernel<SDQ_KEY_U8_MIN>, dim3(rows), dim3(kTkThreads), 0, stream,
                        keys, n, k, n_sink, n_local, idx_out, stride);
   return check_launch("topk_select");
+}
+
+extern "C" int topk_select_block_max(const float* keys, const float* block_max, int rows, int n,
+                                     int k, int n_sink, int n_local, int32_t* idx_out,
+                                     hipStream_t stream) {
+  int stride = 0;
+  const int rc = topk_validate("topk_select_block_max", keys, SDQ_KEY_F32_MAX, rows, n, k, n_sink,
+                               n_local, idx_out, &stride);
+  if (rc != SDQ_OK) return rc;
+  SDQ_REQUIRE(block_max, "topk_select_block_max: null block_max");
+  SDQ_REQUIRE(n % 64 == 0 && n_sink % 64 == 0 && n_local % 64 == 0,
+              "topk_select_block_max: n, n_sink and n_local must be multiples of 64");
+  SDQ_REQUIRE(n / 64 <= kBmMaxBlocks, "topk_select_block_max: n=%d exceeds %d", n, kBmMaxBlocks * 64);
+  SDQ_REQUIRE(reinterpret_cast<uintptr_t>(keys) % 16 == 0, "topk_select_block_max: keys must be 16-byte aligned");
+  if (stride == 0) return SDQ_OK;
+  launch_block_max_select(keys, block_max, rows, n, k, n_sink, n_local, idx_out, stride, stream);
+  return check_launch("topk_select_block_max");
 }

@@ -32,7 +32,8 @@ _SIGS = {
     "fathom_plan": ([_vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp], _c_int),
     "fathom_plan_uniform": ([_vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp], _c_int),
     "fathom_gather": ([_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp], _c_int),
-    "fathom_scan": ([_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp], _c_int),
+    "fathom_scan": ([_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp], _c_int),
+    "topk_select_block_max": ([_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp], _c_int),
     "topk_select_workspace_bytes": ([_c_int, _c_int, _c_int, _c_int], _c_size),
     "topk_select": ([_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _c_size, _vp], _c_int),
     "hamming_scan": ([_vp, _vp, _c_int, _c_int, _vp, _vp], _c_int),
@@ -100,15 +101,26 @@ def _out(t, shape, dtype, device, name, elem):
 
 
 # ------------------------------------------------------------------ ingest
+class PlaneIndex:
+    """The bit-plane index of one layer: planes uint32 [G][128][4][n/32] and
+    meta uint32 [G][128][n/64]."""
+
+    def __init__(self, planes, meta):
+        self.planes, self.meta = planes, meta
+
+    def __iter__(self):
+        return iter((self.planes, self.meta))
+
+
 def fathom_ingest(keys, planes=None, meta=None, stream=None):
-    """keys bf16 [G][n][128] -> (planes uint32 [G][128][4][n/32], meta uint32 [G][128][n/64])."""
+    """keys bf16 [G][n][128] -> PlaneIndex(planes, meta)."""
     G, n, d = keys.shape
     _dev(keys, "keys", 2)
     planes = _out(planes, (G, d, 4, n // 32), torch.int32, keys.device, "planes", 4)
     meta = _out(meta, (G, d, n // 64), torch.int32, keys.device, "meta", 4)
     _check(load().fathom_ingest(_vp(keys.data_ptr()), G, n, d, _vp(planes.data_ptr()),
                                 _vp(meta.data_ptr()), _stream(stream)), "fathom_ingest")
-    return planes, meta
+    return PlaneIndex(planes, meta)
 
 
 def minmax_summarize(keys, block=16, bmin=None, bmax=None, stream=None):
@@ -163,18 +175,39 @@ def fathom_gather(planes_host, meta_host, depth, planes_dev, meta_dev, stream=No
                                 _vp(meta_dev.data_ptr()), _stream(stream)), "fathom_gather")
 
 
-def fathom_scan(planes, meta, depth, qbar, n, scores=None, stream=None):
-    """-> scores float32 [G][n]."""
+def fathom_scan(index, depth, qbar, n, scores=None, block_max=None, planes=None, meta=None,
+                stream=None):
+    """index: PlaneIndex (``planes``/``meta`` override its HBM buffers, e.g. a
+    staging copy filled by fathom_gather) -> scores float32 [G][n]; also fills
+    ``block_max`` float32 [G][n/64] if given."""
     G, d = depth.shape
+    planes = index.planes if planes is None else planes
+    meta = index.meta if meta is None else meta
     _dev(planes, "planes", 4, G * d * 4 * (n // 32))
     _dev(meta, "meta", 4, G * d * (n // 64))
     _dev(depth, "depth", 1, G * d)
     _dev(qbar, "qbar", 4, G * d)
     scores = _out(scores, (G, n), torch.float32, planes.device, "scores", 4)
+    bm = _vp(0)
+    if block_max is not None:
+        bm = _dev(block_max, "block_max", 4, G * (n // 64))
     _check(load().fathom_scan(_vp(planes.data_ptr()), _vp(meta.data_ptr()), _vp(depth.data_ptr()),
-                              _vp(qbar.data_ptr()), G, d, n, _vp(scores.data_ptr()), _stream(stream)),
-           "fathom_scan")
+                              _vp(qbar.data_ptr()), G, d, n, _vp(scores.data_ptr()), bm,
+                              _stream(stream)), "fathom_scan")
     return scores
+
+
+def topk_select_block_max(keys, block_max, k, n_sink=0, n_local=0, idx=None, stream=None):
+    """float32 keys [rows][n] with their 64-key block maxima [rows][n/64] ->
+    idx int32 [rows][k + n_sink + n_local] (as topk_select)."""
+    rows, n = keys.shape
+    _dev(keys, "keys", 4, rows * n)
+    _dev(block_max, "block_max", 4, rows * (n // 64))
+    idx = _out(idx, (rows, k + n_sink + n_local), torch.int32, keys.device, "idx", 4)
+    _check(load().topk_select_block_max(_vp(keys.data_ptr()), _vp(block_max.data_ptr()), rows, n,
+                                        int(k), int(n_sink), int(n_local), _vp(idx.data_ptr()),
+                                        _stream(stream)), "topk_select_block_max")
+    return idx
 
 
 def topk_workspace(rows, n, k, key_type, device="cuda"):

@@ -39,10 +39,10 @@ def test_invalid_arguments_rejected_without_launch():
     null = ctypes.c_void_p(0)
     s = ctypes.c_void_p(0)
     EINVAL = -1
-    assert L.fathom_scan(null, p, p, p, 8, 128, 4096, p, s) == EINVAL
+    assert L.fathom_scan(null, p, p, p, 8, 128, 4096, p, null, s) == EINVAL
     assert b"null" in L.sdq_last_error()
-    assert L.fathom_scan(p, p, p, p, 8, 128, 4000, p, s) == EINVAL          # n % 64
-    assert L.fathom_scan(p, p, p, p, 8, 64, 4096, p, s) == EINVAL           # d != 128
+    assert L.fathom_scan(p, p, p, p, 8, 128, 4000, p, null, s) == EINVAL    # n % 64
+    assert L.fathom_scan(p, p, p, p, 8, 64, 4096, p, null, s) == EINVAL     # d != 128
     assert L.fathom_plan(p, p, 8, 4, 128, -1, p, p, s) == EINVAL             # negative budget
     assert L.fathom_plan_uniform(p, p, 8, 4, 128, 129, p, p, s) == EINVAL    # > d channels
     assert L.fathom_ingest(p, 0, 4096, 128, p, p, s) == EINVAL               # G < 1

@@ -132,10 +132,13 @@ def _scan_case(sdq, G, n, budget, uniform=None):
     case = synth.fathom_case(2, n=n, heads=list(range(G)), with_values=False)
     q = case["q"][:G * 4]
     var = case["var"][:G]
-    planes, meta = sdq.fathom_ingest(dev(case["K"]))
+    index = sdq.fathom_ingest(dev(case["K"]))
     depth, qbar = sdq.fathom_plan(dev(q), dev(var), budget, uniform_channels=uniform)
-    scores = sdq.fathom_scan(planes, meta, depth, qbar, n)
+    bm = torch.empty(G, n // 64, device="cuda")
+    scores = sdq.fathom_scan(index, depth, qbar, n, block_max=bm)
     torch.cuda.synchronize()
+    # block maxima are exactly the maxima of the written scores
+    assert torch.equal(bm, scores.view(G, n // 64, 64).amax(-1))
     rp, rm = o_fathom.ingest(case["K"])
     rd, rq = o_fathom.plan_heads(q, var, 4, budget=budget, n_uniform=uniform)
     ref = o_fathom.scan_heads(rp, rm, rd, rq, n)
@@ -196,6 +199,36 @@ def test_topk_f32_degenerate_rows(sdq):
     keys[0, 99999] = 7.0
     got = host(sdq.topk_select(dev(keys), 9000, 1, 1))
     assert np.array_equal(got, _topk_ref(keys, 9000, 1, 1, True))
+
+
+@pytest.mark.parametrize("rows,n,k,ns,nl", [(8, 1 << 20, 512, 0, 0), (2, 65536 + 128, 64, 64, 64),
+                                            (3, 100032, 1563, 0, 0), (1, 131072, 4096, 0, 0)])
+def test_topk_block_max_bitexact(sdq, rows, n, k, ns, nl):
+    _say(f"topk block-max rows={rows} n={n} k={k}")
+    g = np.random.default_rng(n + 3 * k)
+    keys = (g.standard_normal((rows, n)) * 3).astype(np.float32)
+    keys[:, ::5] = np.round(keys[:, ::5], 1)
+    kt = dev(keys)
+    bm = kt.view(rows, n // 64, 64).amax(-1).contiguous()
+    ref = _topk_ref(keys, k, ns, nl, True)
+    assert np.array_equal(host(sdq.topk_select_block_max(kt, bm, k, ns, nl)), ref)
+    assert np.array_equal(host(sdq.topk_select(kt, k, ns, nl)), ref)
+
+
+def test_topk_block_max_degenerate(sdq):
+    """Ties and clustered maxima that overflow the candidate lists fall back
+    to the exact row path."""
+    _say("topk block-max degenerate rows")
+    n = 1 << 17
+    keys = np.zeros((3, n), np.float32)
+    keys[1, ::64] = 1.0                          # every block has the same maximum
+    keys[2, 64 * 100:64 * 164] = np.arange(64 * 64, dtype=np.float32)   # top keys in 64 blocks
+    kt = dev(keys)
+    bm = kt.view(3, n // 64, 64).amax(-1).contiguous()
+    for k in (1, 512, 2048):
+        ref = _topk_ref(keys, k, 0, 0, True)
+        assert np.array_equal(host(sdq.topk_select_block_max(kt, bm, k)), ref), k
+        assert np.array_equal(host(sdq.topk_select(kt, k)), ref), k
 
 
 @pytest.mark.parametrize("rows,n,k,ns,nl", [(32, 131072, 512, 128, 128), (3, 999, 40, 0, 0),
@@ -303,7 +336,8 @@ def test_fathom_gather_copies_active_prefixes(sdq):
     _say("fathom gather (pinned host -> HBM)")
     G, n = 2, 8192
     case = synth.fathom_case(2, n=n, heads=[0, 1], with_values=False)
-    planes, meta = sdq.fathom_ingest(dev(case["K"]))
+    index = sdq.fathom_ingest(dev(case["K"]))
+    planes, meta = index.planes, index.meta
     depth, qbar = sdq.fathom_plan(dev(case["q"][:8]), dev(case["var"][:2]), 56)
     ph = planes.cpu().pin_memory()
     mh = meta.cpu().pin_memory()
@@ -316,8 +350,8 @@ def test_fathom_gather_copies_active_prefixes(sdq):
         side.wait_event(ev)
         sdq.fathom_gather(ph, mh, depth, pd, md, stream=side)
     torch.cuda.current_stream().wait_stream(side)
-    s_off = sdq.fathom_scan(pd, md, depth, qbar, n)
-    s_on = sdq.fathom_scan(planes, meta, depth, qbar, n)
+    s_off = sdq.fathom_scan(index, depth, qbar, n, planes=pd, meta=md)
+    s_on = sdq.fathom_scan(index, depth, qbar, n)
     torch.cuda.synchronize()
     d = host(depth)
     P, Pd = host(planes, np.uint32), host(pd, np.uint32)
@@ -340,10 +374,12 @@ def _fathom_step(sdq, case, budget, k, uniform=None):
     q = case["q"].reshape(-1, 4, 128)[case["heads"]].reshape(-1, 128)
     var = case["var"][case["heads"]]
     Kd, Vd = dev(case["K"]), dev(case["V"])
-    planes, meta = sdq.fathom_ingest(Kd)
+    index = sdq.fathom_ingest(Kd)
+    planes, meta = index.planes, index.meta
     depth, qbar = sdq.fathom_plan(dev(q), dev(var), budget, uniform_channels=uniform)
-    scores = sdq.fathom_scan(planes, meta, depth, qbar, n)
-    idx = sdq.topk_select(scores, k)
+    bm = torch.empty(G, n // 64, device="cuda")
+    scores = sdq.fathom_scan(index, depth, qbar, n, block_max=bm)
+    idx = sdq.topk_select_block_max(scores, bm, k)
     out = sdq.gather_attend(dev(q.reshape(1, G * 4, 128)), Kd.view(1, G, n, 128),
                             Vd.view(1, G, n, 128), idx.view(1, G, k))
     torch.cuda.synchronize()
@@ -360,9 +396,9 @@ def test_end_to_end_step(sdq, cfg, budget):
     if Hgrp != 4:
         q = case["q"]
         Kd, Vd = dev(case["K"]), dev(case["V"])
-        planes, meta = sdq.fathom_ingest(Kd)
+        index = sdq.fathom_ingest(Kd)
         depth, qbar = sdq.fathom_plan(dev(q), dev(case["var"]), budget)
-        scores = sdq.fathom_scan(planes, meta, depth, qbar, n)
+        scores = sdq.fathom_scan(index, depth, qbar, n)
         idx = sdq.topk_select(scores, k)
         out = sdq.gather_attend(dev(q.reshape(1, G, 128)), Kd.view(1, G, n, 128),
                                 Vd.view(1, G, n, 128), idx.view(1, G, k))
