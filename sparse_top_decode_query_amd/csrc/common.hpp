@@ -65,6 +65,11 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
   return v;
 }
+__device__ __forceinline__ int wave_sum_i32(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
 
 inline unsigned cdiv(size_t a, size_t b) { return unsigned((a + b - 1) / b); }
 

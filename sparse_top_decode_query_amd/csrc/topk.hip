@@ -447,14 +447,31 @@ __global__ __launch_bounds__(kTkThreads) void topk_final_kernel(const float* __r
 // Rows whose competition range is made of whole 64-key blocks.  With M_b the
 // maximum of block b, the k-th largest block maximum T satisfies T <= the
 // k-th largest key (the k blocks whose maxima are >= T hold k keys >= T), so
-// every key of the exact top-k lies in a block with M_b >= T and is >= T
-// itself.  One workgroup per row: select T among the block maxima in LDS,
-// read only the candidate blocks, keep their keys >= T, then select exactly
-// among those (composite key (u, ~index)) and sort the winners by index.
-// Rows where the candidates overflow fall back to the row path.
+// every key of the exact top-k lies in a block with M_b >= T and is >= T.
+// One workgroup per row, no sorting:
+//  1. the block maxima land in LDS (asynchronous global->LDS loads);
+//  2. a 4096-bin histogram of their order-preserving codes over the row's
+//     [min, max] code range locates the bin b* holding the k-th largest
+//     maximum; its lower edge is a float threshold thr <= T, so the top-k
+//     keys are among the keys >= thr;
+//  3. candidate blocks (M_b >= thr) are listed in index order;
+//  4. their keys land in LDS, up to kBmChunk blocks at a time, and the keys
+//     >= thr are listed in index order;
+//  5. the exact k-th largest candidate code and its tie count are found;
+//  6. the winners are written by an index-ordered compaction (ties to the
+//     lower index), so the output comes out ascending.
+// A workgroup issues about one wave instruction per clock, so every pass is
+// kept to a handful of instructions per element (one compare per key once
+// thr is known) and the asynchronous loads keep many reads in flight without
+// unrolled code.  Rows whose candidates overflow the lists fall back to the
+// row path.  Keys must not be NaN.
 constexpr int kBmMaxBlocks = 16384;     // block maxima held in LDS (n <= 2^20)
-constexpr int kBmCandBlocks = 2048;     // candidate blocks read
-constexpr int kBmCap = 4096;            // candidate keys
+constexpr int kBmBins = 4096;
+constexpr int kBmCandBlocks = 2048;     // candidate blocks
+constexpr int kBmCap = 2048;            // candidate keys
+constexpr int kBmChunk = 520;           // candidate blocks landed per round
+constexpr int kBmLand = kBmChunk * 64;  // floats: maxima + histogram, then landed blocks
+static_assert(kBmLand >= kBmMaxBlocks + kBmBins, "landing area holds the maxima and the bins");
 
 __global__ __launch_bounds__(256) void topk_block_max_kernel(const float* __restrict__ keys, int n,
                                                              int nb, float* __restrict__ bm) {
@@ -467,150 +484,268 @@ __global__ __launch_bounds__(256) void topk_block_max_kernel(const float* __rest
   if ((threadIdx.x & 63) == 0) bm[size_t(row) * nb + b] = v;
 }
 
+// Number of set bits of a wave mask in the lanes below this one.
+__device__ __forceinline__ int lane_rank(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
+}
+
+// Asynchronous global->LDS loads of 4 or 16 bytes per lane; `lds` is the
+// wave-uniform base and lane l's bytes land at lds + 4 l or lds + 16 l.
+__device__ __forceinline__ void load_lds_4(const float* g, float* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+}
+__device__ __forceinline__ void load_lds_16(const float* g, float* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// Inverse of f32_order_key on the codes of non-NaN floats (+0 for the code
+// of zero).
+__device__ __forceinline__ float f32_from_order_key(uint32_t c) {
+  return __uint_as_float((c & 0x80000000u) ? (c & 0x7FFFFFFFu) : ~c);
+}
+
+// Block-wide exclusive prefix sum of one counter (512 threads).
+__device__ __forceinline__ int block_scan1(int a, int& total, int* s_scan) {
+  int ea, eb, tb;
+  block_scan2(a, 0, ea, eb, total, tb, s_scan);
+  return ea;
+}
+
 __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __restrict__ keys,
                                                              const float* __restrict__ bm, int n,
                                                              int nb, int k, int n_sink, int n_local,
                                                              int32_t* __restrict__ out, int stride) {
-  __shared__ uint32_t bmc[kBmMaxBlocks];      // block-max codes; reused for the winners' indices
-  __shared__ int cb[kBmCandBlocks];
-  __shared__ uint64_t cand[kBmCap];
-  __shared__ uint32_t hist[256];
-  __shared__ int sh_ncb, sh_ncand;
-  const int row = blockIdx.x, tid = threadIdx.x;
+  __shared__ float land[kBmLand];
+  __shared__ int cb[kBmCandBlocks];       // candidate block numbers
+  __shared__ float ckey[kBmCap];
+  __shared__ int cidx[kBmCap];
+  __shared__ int s_cnt[kBmChunk];         // kept keys per landed block, then offsets
+  __shared__ uint32_t s_red[2 * kTkWaves];
+  __shared__ int s_scan[2 * kTkWaves];
+  __shared__ int s_wsum[kTkWaves];
+  __shared__ uint32_t s_thr;
+  uint32_t* sbin = reinterpret_cast<uint32_t*>(land + kBmMaxBlocks);   // after the maxima
+  uint32_t* hist = reinterpret_cast<uint32_t*>(land);                  // step 5, after landing
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int32_t* o = out + size_t(row) * stride;
   const int lo = n_sink, hi = n - n_local, m = hi - lo;
   const int blo = lo / 64, nbc = m / 64;        // competition blocks [blo, blo + nbc)
   const int K = k < m ? k : m;
   const size_t base = size_t(row) * n;
-  if (K == m || K == 0 || K > nbc || K > kBmCap) {
+  if (K == m || K == 0 || K > nbc) {
     topk_row<SDQ_KEY_F32_MAX>(keys, base, n, k, n_sink, n_local, o, stride);
     return;
   }
-  // 1. block-max codes (8 loads in flight per thread)
-  for (int b0 = 0; b0 < nbc; b0 += 8 * kTkThreads) {
-    float v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int b = b0 + u * kTkThreads + tid;
-      v[u] = b < nbc ? bm[size_t(row) * nb + blo + b] : 0.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int b = b0 + u * kTkThreads + tid;
-      if (b < nbc) bmc[b] = f32_order_key(v[u]);
+  // 1. block maxima into LDS; loads past the row end are clamped
+  {
+    const float* brow = bm + size_t(row) * nb + blo;
+#pragma unroll 1
+    for (int j = wave; j * 64 < nbc; j += kTkWaves) {
+      const int b = j * 64 + lane;
+      load_lds_4(brow + (b < nbc ? b : nbc - 1), land + j * 64);
     }
   }
-  if (tid == 0) {
-    sh_ncb = 0;
-    sh_ncand = 0;
+  for (int i = tid; i < kBmBins; i += kTkThreads) sbin[i] = 0;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  uint32_t cmin = 0xFFFFFFFFu, cmax = 0u;
+#pragma unroll 4
+  for (int b = tid; b < nbc; b += kTkThreads) {
+    const uint32_t c = f32_order_key(land[b]);
+    cmin = c < cmin ? c : cmin;
+    cmax = c > cmax ? c : cmax;
+  }
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) {
+    const uint32_t x = __shfl_xor(cmin, s, 64), y = __shfl_xor(cmax, s, 64);
+    cmin = x < cmin ? x : cmin;
+    cmax = y > cmax ? y : cmax;
+  }
+  if (lane == 0) {
+    s_red[wave] = cmin;
+    s_red[kTkWaves + wave] = cmax;
   }
   __syncthreads();
-  // 2. K-th largest block-max code
-  __shared__ uint32_t s_red[2 * kTkWaves];
-  const uint32_t T = select_kth(
-                         nbc, K,
-                         [&](int i, uint32_t* u) {
-                           *u = bmc[i];
-                           return true;
-                         },
-                         hist, s_red)
-                         .T;
-  // 3. candidate blocks
-  for (int b0 = 0; b0 < nbc; b0 += kTkThreads) {
-    const int b = b0 + tid;
-    const int slot = wave_append(b < nbc && bmc[b] >= T, &sh_ncb);
-    if (slot >= 0 && slot < kBmCandBlocks) cb[slot] = blo + b;
+  cmin = 0xFFFFFFFFu;
+  cmax = 0u;
+#pragma unroll
+  for (int w = 0; w < kTkWaves; ++w) {
+    cmin = s_red[w] < cmin ? s_red[w] : cmin;
+    cmax = s_red[kTkWaves + w] > cmax ? s_red[kTkWaves + w] : cmax;
+  }
+  // bins of width 2^sh over [cmin, cmax]: (cmax - cmin) >> sh < kBmBins
+  const int wbits = 32 - __clz(cmax - cmin);
+  const int sh = wbits > 12 ? wbits - 12 : 0;
+  // 2. histogram of the block-maximum codes; bin b* holding the K-th largest
+#pragma unroll 4
+  for (int b = tid; b < nbc; b += kTkThreads)
+    atomicAdd(&sbin[(f32_order_key(land[b]) - cmin) >> sh], 1u);
+  __syncthreads();
+  {
+    // thread t owns bins 8t..8t+7; suffix sums from the top
+    constexpr int BT = kBmBins / kTkThreads;
+    int c[BT], lsum = 0;
+#pragma unroll
+    for (int e = 0; e < BT; ++e) {
+      c[e] = sbin[BT * tid + e];
+      lsum += c[e];
+    }
+    int tot;
+    const int before = block_scan1(lsum, tot, s_scan);
+    int above = tot - before - lsum;                     // maxima in higher threads' bins
+#pragma unroll
+    for (int e = BT - 1; e >= 0; --e) {
+      if (above < K && above + c[e] >= K) s_thr = cmin + (uint32_t(BT * tid + e) << sh);
+      above += c[e];
+    }
   }
   __syncthreads();
-  const int ncb = sh_ncb;
+  const float thr = f32_from_order_key(s_thr);   // v >= thr  <=>  bin(v) >= b*
+  // 3. candidate blocks in index order.  Wave w covers blocks
+  //    [w * BPW, (w + 1) * BPW) in rounds of 64 (lane = block); ballots give
+  //    the in-wave order.
+  constexpr int BPW = kBmMaxBlocks / kTkWaves;
+  uint32_t flags = 0;
+  int wcount = 0;
+#pragma unroll 4
+  for (int u = 0; u < BPW / 64; ++u) {
+    const int b = wave * BPW + u * 64 + lane;
+    const bool f = b < nbc && land[b] >= thr;
+    flags |= uint32_t(f) << u;
+    wcount += __popcll(__ballot(f));
+  }
+  if (lane == 0) s_wsum[wave] = wcount;
+  __syncthreads();
+  int ncb = 0, woff = 0;
+#pragma unroll
+  for (int w = 0; w < kTkWaves; ++w) {
+    woff += w < wave ? s_wsum[w] : 0;
+    ncb += s_wsum[w];
+  }
   if (ncb > kBmCandBlocks) {
     topk_row<SDQ_KEY_F32_MAX>(keys, base, n, k, n_sink, n_local, o, stride);
     return;
   }
-  // 4. candidate keys: (block, 16-byte part) items, four loads in flight per
-  // thread before any is used
-  const int items = ncb * 16;
-  for (int it0 = 0; it0 < items; it0 += 4 * kTkThreads) {
-    float4 v[4];
-    int e0[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int it = it0 + u * kTkThreads + tid;
-      e0[u] = it < items ? cb[it >> 4] * 64 + (it & 15) * 4 : -1;
-      v[u] = e0[u] >= 0 ? *reinterpret_cast<const float4*>(keys + base + e0[u])
-                        : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float vv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t uc = e0[u] >= 0 ? f32_order_key(vv[e]) : 0u;
-        const int slot = wave_append(e0[u] >= 0 && uc >= T, &sh_ncand);
-        if (slot >= 0 && slot < kBmCap) cand[slot] = (uint64_t(uc) << 32) | uint64_t(~uint32_t(e0[u] + e));
-      }
-    }
+#pragma unroll 4
+  for (int u = 0; u < BPW / 64; ++u) {
+    const bool f = (flags >> u) & 1u;
+    const uint64_t mk = __ballot(f);
+    if (f) cb[woff + lane_rank(mk)] = wave * BPW + u * 64 + lane;
+    woff += __popcll(mk);
   }
   __syncthreads();
-  const int nc = sh_ncand;
-  if (nc > kBmCap) {
+  // 4. candidate keys in index order, kBmChunk blocks per landing round.  A
+  //    16-byte load per lane lands four blocks per wave instruction; landed
+  //    block i is then counted and written by wave i % 8: pass A counts the
+  //    keys >= thr per block, a prefix sum turns counts into offsets, pass B
+  //    writes the kept keys at offset + in-wave rank.
+  int nc = 0;
+#pragma unroll 1
+  for (int c0 = 0; c0 < ncb; c0 += kBmChunk) {
+    const int nch = ncb - c0 < kBmChunk ? ncb - c0 : kBmChunk;
+#pragma unroll 1
+    for (int q = wave; q * 4 < nch; q += kTkWaves) {
+      int i = q * 4 + (lane >> 4);
+      i = i < nch ? i : nch - 1;                 // clamped: the spare lanes reload a block
+      load_lds_16(keys + base + size_t(blo + cb[c0 + i]) * 64 + (lane & 15) * 4, land + q * 256);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll 4
+    for (int i = wave; i < nch; i += kTkWaves) {
+      const int cnt = __popcll(__ballot(land[i * 64 + lane] >= thr));
+      if (lane == 0) s_cnt[i] = cnt;
+    }
+    __syncthreads();
+    {
+      constexpr int PT = (kBmChunk + kTkThreads - 1) / kTkThreads;
+      int cnt[PT], sum = 0;
+#pragma unroll
+      for (int e = 0; e < PT; ++e) {
+        const int i = tid * PT + e;
+        cnt[e] = i < nch ? s_cnt[i] : 0;
+        sum += cnt[e];
+      }
+      int tot;
+      int off = nc + block_scan1(sum, tot, s_scan);
+#pragma unroll
+      for (int e = 0; e < PT; ++e) {
+        const int i = tid * PT + e;
+        if (i < nch) s_cnt[i] = off;
+        off += cnt[e];
+      }
+      nc += tot;
+    }
+    __syncthreads();
+    if (nc <= kBmCap) {
+#pragma unroll 2
+      for (int i = wave; i < nch; i += kTkWaves) {
+        const float v = land[i * 64 + lane];
+        const bool f = v >= thr;
+        const uint64_t mk = __ballot(f);
+        if (f) {
+          const int pos = s_cnt[i] + lane_rank(mk);
+          ckey[pos] = v;
+          cidx[pos] = (blo + cb[c0 + i]) * 64 + lane;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (nc > kBmCap || nc < K) {
     topk_row<SDQ_KEY_F32_MAX>(keys, base, n, k, n_sink, n_local, o, stride);
     return;
   }
-  // 5. exact selection among the candidates: the K-th largest code T2 and
-  // how many codes equal to T2 to keep, then among those the lowest indices
-  const KthResult k2 = select_kth(
+  // 5. exact K-th largest candidate code and how many of its ties to keep
+  const KthResult kr = select_kth(
       nc, K,
       [&](int i, uint32_t* u) {
-        *u = uint32_t(cand[i] >> 32);
+        *u = f32_order_key(ckey[i]);
         return true;
       },
       hist, s_red);
-  uint32_t idx_cut = 0;            // largest ~index kept among codes equal to T2
-  {
-    const KthResult k3 = select_kth(
-        nc, k2.need,
-        [&](int i, uint32_t* u) {
-          const uint64_t v = cand[i];
-          *u = uint32_t(v);
-          return uint32_t(v >> 32) == k2.T;
-        },
-        hist, s_red);
-    idx_cut = k3.T;
-  }
-  const uint64_t pre = (uint64_t(k2.T) << 32) | idx_cut;   // exactly K composites are >= pre
-  // 6. winners sorted by index (bitonic over the next power of two)
-  int* widx = reinterpret_cast<int*>(bmc);
-  if (tid == 0) sh_ncb = 0;
-  __syncthreads();
-  for (int i0 = 0; i0 < nc; i0 += kTkThreads) {
-    const int i = i0 + tid;
-    const bool win = i < nc && cand[i] >= pre;
-    const int slot = wave_append(win, &sh_ncb);
-    if (slot >= 0 && slot < kBmCap) widx[slot] = int(~uint32_t(cand[i]));
-  }
-  int P = 1;
-  while (P < K) P <<= 1;
-  __syncthreads();
-  for (int i = K + tid; i < P; i += kTkThreads) widx[i] = 0x7FFFFFFF;
-  __syncthreads();
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int st = size >> 1; st > 0; st >>= 1) {
-      for (int t = tid; t < P / 2; t += kTkThreads) {
-        const int i = 2 * t - (t & (st - 1));
-        const int j = i + st;
-        const bool up = (i & size) == 0;
-        const int a = widx[i], b = widx[j];
-        if ((a > b) == up) {
-          widx[i] = b;
-          widx[j] = a;
+  // 6. winners in index order (candidates are already ordered by index)
+  write_fixed(o, n, n_sink, n_local, K, stride);
+  int out_pos = n_sink, eq_seen = 0;
+  constexpr int IPT = 4;
+  for (int c0 = 0; c0 < nc; c0 += kTkThreads * IPT) {
+    const int i0 = c0 + tid * IPT;
+    uint32_t u[IPT];
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int e = 0; e < IPT; ++e) {
+      const int i = i0 + e;
+      u[e] = i < nc ? f32_order_key(ckey[i]) : 0u;
+      if (i < nc) {
+        gt += u[e] > kr.T;
+        eq += u[e] == kr.T;
+      }
+    }
+    int egt, eeq, tgt, teq;
+    block_scan2(gt, eq, egt, eeq, tgt, teq, s_scan);
+    const int eq_left = kr.need - eq_seen > 0 ? kr.need - eq_seen : 0;
+    int pos = out_pos + egt + (eeq < eq_left ? eeq : eq_left);
+    int my_eq = eeq;
+    const int end = n_sink + K;
+#pragma unroll
+    for (int e = 0; e < IPT; ++e) {
+      const int i = i0 + e;
+      if (i < nc) {
+        if (u[e] > kr.T) {
+          if (pos < end) o[pos] = cidx[i];
+          ++pos;
+        } else if (u[e] == kr.T) {
+          if (my_eq < eq_left) {
+            if (pos < end) o[pos] = cidx[i];
+            ++pos;
+          }
+          ++my_eq;
         }
       }
-      __syncthreads();
     }
+    out_pos += tgt + (teq < eq_left ? teq : eq_left);
+    eq_seen += teq;
   }
-  write_fixed(o, n, n_sink, n_local, K, stride);
-  for (int i = tid; i < K; i += kTkThreads) o[n_sink + i] = widx[i];
 }
 
 }  // namespace sdq
@@ -625,7 +760,7 @@ static bool use_fast(int n, int n_sink, int n_local, int k, int key_type) {
 static bool use_block_max(int n, int n_sink, int n_local, int k, int key_type) {
   const int m = n - n_sink - n_local;
   return key_type == SDQ_KEY_F32_MAX && m >= kFastMinComp && n % 64 == 0 && n_sink % 64 == 0 &&
-         n_local % 64 == 0 && n / 64 <= kBmMaxBlocks && k < m && k <= kBmCap && k <= m / 64;
+         n_local % 64 == 0 && n / 64 <= kBmMaxBlocks && k < m && k <= m / 64;
 }
 
 extern "C" size_t topk_select_workspace_bytes(int rows, int n, int k, int key_type) {
