@@ -1,0 +1,415 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the sparse attention hot path on one GPU.
+
+The timed step is one decode step of one layer of the bit-plane index at a
+1,048,576-token context: 8 KV heads x 4 query heads (GQA), d = 128, a read
+plan of B = 56 plane bits per KV head, k = 512 selected rows per KV head:
+
+    fathom_plan -> fathom_scan (+ 64-token block maxima)
+                -> topk_select_block_max -> gather_attend
+
+All inputs are seeded synthetic data (synth.fathom_case(3)) resident in HBM
+before timing starts.  Eight copies of the plane index rotate between steps
+so the 256 MB last-level cache cannot serve the index from one step to the
+next (a real decode step reads each layer's index once).
+
+Output: one JSON line.  `value` is keys scored per second over the whole
+step (n * G / step time).  `roofline` prices the dominant kernel
+(fathom_scan) against HBM: algorithmic bytes per launch (plane-prefix bits,
+one scale/offset word per active channel per 64-token block, the fp32 score
+write) over its average launch time, measured with HIP events on the stream
+the kernels run on.  `roofline_valu` prices the same launches against the
+vector ALU (one weighted accumulate per plane bit per token).
+`cpu_baseline` is the CPU oracle (fp64 NumPy) timed on the host on the same
+1M-token workload, one KV head at a time.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu] [--no-extras]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sparse decode-step µs & keys scored/s at 1M ctx; % of HBM/VALU roofline"
+HBM_PEAK_GBS = 8000.0                          # MI355X HBM3E
+VALU_PEAK_OPS = 256 * 64 * 2.4e9               # 256 CUs x 64 lanes x 2.4 GHz, one op per lane-cycle
+N_COPIES = 8                                   # rotating copies of the plane index (4.6 GB)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fathom_scan_n1M_G8_B56.traffic.txt")
+SCAN_SOURCE = os.path.join(ROOT, "sparse_top_decode_query_amd", "csrc", "scan.hip")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--budget", type=int, default=56, help="plane bits per KV head")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the plan variants, the host-resident index and configs 4/5")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run plain 512 MiB device copies (for counter calibration)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def pct(xs, p):
+    xs = sorted(xs)
+    i = min(len(xs) - 1, max(0, int(round(p / 100.0 * (len(xs) - 1)))))
+    return xs[i]
+
+
+def scan_traffic(depth_rows_key):
+    """HBM bytes per fathom_scan launch from the committed counter summary,
+    if it was taken on the current scan source with the same plan."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
+        kv = {k.strip(): v.strip() for k, v in kv.items()}
+        with open(SCAN_SOURCE, "rb") as f:
+            src = hashlib.sha256(f.read()).hexdigest()
+        if kv.get("scan_source_sha256") != src or kv.get("plan_sha256") != depth_rows_key:
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------------ CPU oracle
+def cpu_baseline(budget, k, min_seconds=10.0, max_passes=50):
+    """The CPU oracle's plan + scan + top-k + attention on the same 1M-token
+    layer, one KV head at a time; the index is built once, untimed, and
+    passes over all KV heads repeat until at least `min_seconds` of timed
+    work."""
+    import synth
+    from oracle import attend as o_attend
+    from oracle import fathom as o_fathom
+    from oracle import select as o_select
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(1)
+    except ImportError:                                        # pragma: no cover
+        limiter = None
+    c = synth.CONFIGS[3]
+    G, Hgrp = c["G"], c["Hgrp"]
+    heads = []
+    for g in range(G):
+        case = synth.fathom_case(3, heads=[g])
+        planes, meta = o_fathom.ingest(case["K"])
+        heads.append((case["n"], planes, meta, case["q"][g * Hgrp:(g + 1) * Hgrp],
+                      case["var"][g:g + 1], case["K"], case["V"]))
+    log("cpu oracle: index built for every KV head")
+    timed, keys, passes = 0.0, 0, 0
+    while timed < min_seconds and passes < max_passes:
+        for n, planes, meta, q, var, K, V in heads:
+            t0 = time.perf_counter()
+            depth, qbar = o_fathom.plan_heads(q, var, Hgrp, budget=budget)
+            s = o_fathom.scan_heads(planes, meta, depth, qbar, n)
+            idx = o_select.topk(s[0], k)
+            o_attend.attend(q[None], K[None], V[None], idx[None, None])
+            timed += time.perf_counter() - t0
+            keys += n
+        passes += 1
+        log(f"cpu oracle: pass {passes}: {timed:.1f} s timed so far")
+    if limiter is not None:
+        limiter.unregister()
+    return {
+        "value": keys / timed, "unit": "keys/s", "cores": 1, "kind": "oracle",
+        "sample": (f"{passes} passes over all {G} KV heads at n=1048576 (4 query heads each, "
+                   f"B={budget}, k={k}): plan+scan+top-k+attention per head, fp64 NumPy, one thread; "
+                   f"index build untimed; host has {os.cpu_count()} logical CPUs"),
+        "seconds": round(timed, 2),
+    }
+
+
+# ------------------------------------------------------------------ GPU
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: the decode step shards by KV head with no "
+              "exchange, so the per-GPU figure is the N=1 line (run without --gpus).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from sparse_top_decode_query_amd import bytemodel, lib
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    lib.load()                                   # raises if the HIP library is not built
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+
+    c = synth.CONFIGS[3]
+    G, Hgrp, n, k, B = c["G"], c["Hgrp"], c["n"], c["k"], args.budget
+    t0 = time.time()
+    case = synth.fathom_case(3)
+    log(f"generated the 1M-token layer in {time.time() - t0:.1f} s")
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(dev)
+
+    K, V = to_dev(case["K"]), to_dev(case["V"])
+    q, var = to_dev(case["q"]), to_dev(case["var"])
+    index = lib.fathom_ingest(K)
+    P = [index.planes] + [index.planes.clone() for _ in range(N_COPIES - 1)]
+    M = [index.meta] + [index.meta.clone() for _ in range(N_COPIES - 1)]
+    depth, qbar = lib.fathom_plan(q, var, B)
+    scores = torch.empty(G, n, device=dev)
+    bmax = torch.empty(G, n // 64, device=dev)
+    idx = torch.empty(G, k, dtype=torch.int32, device=dev)
+    out = torch.empty(1, G * Hgrp, 128, device=dev)
+    ws = lib.attend_workspace(1, G * Hgrp, G, False, k, 1, dev)
+    q3, K4, V4, idx3 = q.view(1, G * Hgrp, 128), K.view(1, G, n, 128), V.view(1, G, n, 128), idx.view(1, G, k)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        if ev:
+            ev[0].record()
+        lib.fathom_plan(q, var, B, depth=depth, qbar=qbar)
+        if ev:
+            ev[1].record()
+        lib.fathom_scan(index, depth, qbar, n, planes=P[i % N_COPIES], meta=M[i % N_COPIES],
+                        scores=scores, block_max=bmax)
+        if ev:
+            ev[2].record()
+        lib.topk_select_block_max(scores, bmax, k, idx=idx)
+        if ev:
+            ev[3].record()
+        lib.gather_attend(q3, K4, V4, idx3, out=out, ws=ws)
+        if ev:
+            ev[4].record()
+
+    # warmup
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, every stage bracketed by events on the launch stream
+    Ksteps = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(Ksteps)]
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e_start.record()
+    for i in range(Ksteps):
+        step(i, evs[i])
+    e_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_per_step = e_start.elapsed_time(e_end) / Ksteps
+    step_us = [e[0].elapsed_time(e[4]) * 1e3 for e in evs]
+    stage_us = {name: statistics.mean(e[a].elapsed_time(e[a + 1]) * 1e3 for e in evs)
+                for a, name in enumerate(("plan", "scan", "topk", "attend"))}
+
+    # roofline of the scan from the actual plan
+    d_rows = depth.cpu().numpy()
+    plan_key = hashlib.sha256(d_rows.tobytes()).hexdigest()
+    scan_bytes = bytemodel.plane_scan_bytes(n, d_rows)
+    scan_ops = bytemodel.plane_scan_bit_ops(n, d_rows)
+    scan_s = stage_us["scan"] * 1e-6
+    t_hbm = scan_bytes / (HBM_PEAK_GBS * 1e9)
+    t_valu = scan_ops / VALU_PEAK_OPS
+    achieved_gbs = scan_bytes / scan_s / 1e9
+    roofline = {
+        "bound": "hbm" if t_hbm >= t_valu else "alu",
+        "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+        "traffic": scan_traffic(plan_key),
+        "kernel": "fathom_scan", "bytes_per_launch": scan_bytes,
+        "launch_us": round(stage_us["scan"], 2),
+        "floor_us": round(max(t_hbm, t_valu) * 1e6, 2),
+        "frac_of_binding_floor": round(max(t_hbm, t_valu) / scan_s, 4),
+    }
+    roofline_valu = {
+        "bound": "alu", "achieved": round(scan_ops / scan_s / 1e12, 3),
+        "peak": round(VALU_PEAK_OPS / 1e12, 1), "unit": "Tops/s (plane-bit accumulates)",
+        "frac": round(scan_ops / scan_s / VALU_PEAK_OPS, 4), "ops_per_launch": scan_ops,
+    }
+    plan_bits = int(d_rows.sum())
+    active = int((d_rows > 0).sum())
+    log(f"step {ms_per_step * 1e3:.1f} us; stages {stage_us}; scan {achieved_gbs:.0f} GB/s")
+
+    extras = {}
+    if not args.no_extras:
+        extras = run_extras(torch, np, lib, bytemodel, synth, dev, case, K4, V4, q, var, q3, index,
+                            P, M, n, G, Hgrp, k)
+    if args.copy_calibration:
+        # a plain elementwise copy of known size (multiply by one: 512 MiB read, 512 MiB written)
+        src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        extras["copy_calibration_bytes"] = src.numel() * 4
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(B, k)
+
+    keys = n * G
+    result = {
+        "metric": METRIC,
+        "value": keys / (ms_per_step * 1e-3),
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": Ksteps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"bit-plane decode step, 1 layer: {G} KV heads x {Hgrp} query heads, d=128, "
+                         f"n={n} tokens, read plan B={B} plane bits/KV head, k={k}, index in HBM"),
+            "n": n, "kv_heads": G, "q_heads": G * Hgrp, "budget_bits": B, "k": k,
+            "plan_bits_total": plan_bits, "active_channels_total": active,
+            "plan_sha256": plan_key,
+        },
+        "roofline": roofline,
+        "roofline_valu": roofline_valu,
+        "cpu_baseline": cpu,
+        "step_us": {"mean": round(ms_per_step * 1e3, 2), "p10": round(pct(step_us, 10), 2),
+                    "p50": round(pct(step_us, 50), 2), "p90": round(pct(step_us, 90), 2)},
+        "stage_us": {k_: round(v, 2) for k_, v in stage_us.items()},
+        "keys_scored_per_s_scan": keys / scan_s,
+        "host_wall_s_timed_region": round(wall, 4),
+        "extras": extras,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def timeit(torch, fn, reps=30, warm=3):
+    for i in range(warm):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def run_extras(torch, np, lib, bytemodel, synth, dev, case, K4, V4, q, var, q3, index, P, M, n, G,
+               Hgrp, k):
+    """Context numbers: other read plans, the host-resident index, configs 4 and 5."""
+    ex = {}
+    c = synth.CONFIGS[3]
+    scores = torch.empty(G, n, device=dev)
+    bmax = torch.empty(G, n // 64, device=dev)
+    for B in list(c["budgets"]) + [None]:
+        if B is None:
+            depth, qbar = lib.fathom_plan(q, var, 0, uniform_channels=c["uniform_channels"])
+            name = f"uniform_{c['uniform_channels']}x4"
+        else:
+            depth, qbar = lib.fathom_plan(q, var, B)
+            name = f"B{B}"
+        us = timeit(torch, lambda i: lib.fathom_scan(index, depth, qbar, n, planes=P[i % len(P)],
+                                                     meta=M[i % len(M)], scores=scores, block_max=bmax))
+        d_rows = depth.cpu().numpy()
+        nbytes = bytemodel.plane_scan_bytes(n, d_rows)
+        ex[f"scan_{name}"] = {"us": round(us, 2), "bytes": nbytes,
+                              "hbm_frac": round(nbytes / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
+                              "valu_frac": round(bytemodel.plane_scan_bit_ops(n, d_rows) / (us * 1e-6) / VALU_PEAK_OPS, 4)}
+        log(f"extras: scan {name} {us:.1f} us")
+    ws_t = lib.topk_workspace(G, n, k, lib.SDQ_KEY_F32_MAX, dev)
+    idx = torch.empty(G, k, dtype=torch.int32, device=dev)
+    ex["topk_select_generic_us"] = round(timeit(torch, lambda i: lib.topk_select(scores, k, idx=idx, ws=ws_t)), 2)
+
+    # host-resident index: gather the active prefixes into HBM, then scan
+    depth, qbar = lib.fathom_plan(q, var, 56)
+    planes_h = torch.empty(index.planes.shape, dtype=index.planes.dtype, pin_memory=True)
+    meta_h = torch.empty(index.meta.shape, dtype=index.meta.dtype, pin_memory=True)
+    planes_h.copy_(index.planes)
+    meta_h.copy_(index.meta)
+    stage_p, stage_m = torch.zeros_like(index.planes), torch.zeros_like(index.meta)
+    torch.cuda.synchronize()
+    moved = bytemodel.plane_scan_read_bytes(n, depth.cpu().numpy())
+    us = timeit(torch, lambda i: lib.fathom_gather(planes_h, meta_h, depth, stage_p, stage_m), reps=5, warm=1)
+    ex["offload_gather_B56"] = {"us": round(us, 1), "bytes": moved, "GB_per_s": round(moved / (us * 1e-6) / 1e9, 1)}
+    log(f"extras: host gather {us:.0f} us")
+    del planes_h, meta_h, stage_p, stage_m
+
+    # config 4: Hamming signatures -> top-512 + 128 sink + 128 local -> attention per query head
+    h = synth.hamming_case(4)
+    sigs, qsig = torch.from_numpy(h["sigs"].view(np.int32)).to(dev), torch.from_numpy(h["qsig"].view(np.int32)).to(dev)
+    Kh = torch.from_numpy(h["K"].view(np.int16)).to(dev)[None]
+    Vh = torch.from_numpy(h["V"].view(np.int16)).to(dev)[None]
+    qh = torch.from_numpy(h["q"]).to(dev)[None]
+    dist = torch.empty(h["H"], h["n"], dtype=torch.uint8, device=dev)
+    m_tot = h["m"] + h["sink"] + h["local"]
+    idx_h = torch.empty(h["H"], m_tot, dtype=torch.int32, device=dev)
+    out_h = torch.empty(1, h["H"], 128, device=dev)
+    ws_h = lib.topk_workspace(h["H"], h["n"], h["m"], lib.SDQ_KEY_U8_MIN, dev)
+    ws_a = lib.attend_workspace(1, h["H"], h["Hkv"], True, m_tot, 1, dev)
+
+    def hstep(i):
+        lib.hamming_scan(sigs, qsig, dist=dist)
+        lib.topk_select(dist, h["m"], h["sink"], h["local"], idx=idx_h, ws=ws_h)
+        lib.gather_attend(qh, Kh, Vh, idx_h[None], per_query_head=True, out=out_h, ws=ws_a)
+    us_step = timeit(torch, hstep)
+    us_scan = timeit(torch, lambda i: lib.hamming_scan(sigs, qsig, dist=dist))
+    hb = bytemodel.hamming_scan_bytes(h["n"], h["H"])
+    ex["hamming_cfg4"] = {"step_us": round(us_step, 2), "scan_us": round(us_scan, 2),
+                          "keys_scored_per_s_step": h["n"] * h["H"] / (us_step * 1e-6),
+                          "scan_hbm_frac": round(hb / (us_scan * 1e-6) / (HBM_PEAK_GBS * 1e9), 4)}
+    log(f"extras: hamming step {us_step:.1f} us")
+    del sigs, Kh, Vh, dist
+
+    # config 5: min/max block summaries, 64 requests -> top 128 blocks + local -> attention
+    mm = synth.minmax_case(5)
+    R, Gm, nm = mm["R"], mm["G"], mm["n"]
+    Km = torch.from_numpy(mm["K"].reshape(R * Gm, nm, 128).view(np.int16)).to(dev)
+    Vm = torch.from_numpy(mm["V"].view(np.int16)).to(dev)
+    qm = torch.from_numpy(mm["q"]).to(dev)
+    bmin, bmax_s = lib.minmax_summarize(Km, 16)
+    nbk = nm // 16
+    S = torch.empty(R * Gm, nbk, device=dev)
+    kb = mm["top_blocks"]
+    idx_m = torch.empty(R * Gm, kb + 1, dtype=torch.int32, device=dev)
+    out_m = torch.empty(R, Gm * mm["Hgrp"], 128, device=dev)
+    ws_m = lib.topk_workspace(R * Gm, nbk, kb, lib.SDQ_KEY_F32_MAX, dev)
+    ws_am = lib.attend_workspace(R, Gm * mm["Hgrp"], Gm, False, kb + 1, 16, dev)
+    qflat = qm.reshape(-1, 128)
+    Kmv = Km.view(R, Gm, nm, 128)
+
+    def mstep(i):
+        lib.minmax_block_scan(bmin, bmax_s, qflat, scores=S)
+        lib.topk_select(S, kb, 0, 1, idx=idx_m, ws=ws_m)
+        lib.gather_attend(qm, Kmv, Vm, idx_m.view(R, Gm, -1), block_tokens=16, out=out_m, ws=ws_am)
+    us_step = timeit(torch, mstep, reps=20)
+    us_scan = timeit(torch, lambda i: lib.minmax_block_scan(bmin, bmax_s, qflat, scores=S), reps=20)
+    mb = bytemodel.minmax_scan_bytes(nbk, R * Gm)
+    ex["minmax_cfg5"] = {"step_us": round(us_step, 2), "scan_us": round(us_scan, 2),
+                         "keys_scored_per_s_step": nm * R * Gm / (us_step * 1e-6),
+                         "scan_hbm_frac": round(mb / (us_scan * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
+                         "attend_bytes": bytemodel.attend_bytes((kb + 1) * 16, R * Gm)}
+    log(f"extras: minmax step {us_step:.1f} us")
+    return ex
+
+
+if __name__ == "__main__":
+    main()
