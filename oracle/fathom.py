@@ -13,7 +13,7 @@ Caches -- summary page):
     spread over channels (0 to 4 bits each) by this marginal gain; the query
     heads under one KV head share one plan.
 
-Readings taken where the page is silent (each is listed in the design doc):
+Readings taken where the page is silent:
   * the quantiser is asymmetric: offset = fp16(block min), scale =
     fp16((max - min) / 15), code = clamp(rint((x - offset) / scale), 0, 15),
     all in float32, code 0 when the scale is 0;
