@@ -12,13 +12,12 @@
 // plane row is read as 64 consecutive dwords per wave (256-byte coalesced
 // vector loads, each byte once), and the lane's 32 tokens share one 64-token
 // block, so the weights w_bj are per-lane values.  Tokens i and i+16 of the
-// word are handled together: two bit operations per plane move their t-bit
-// codes into the low and high 16-bit halves of one register, and a code
-// pattern c read as an fp16 is the denormal c * 2^-24 -- exact -- so one
-// v_fma_mix_f32 per token and channel adds c * (w_bj * 2^(24+4-t)) to a
-// float32 accumulator.  That is t+1 instructions per token and channel
-// instead of one extract and one multiply-add per bit.  The float32 constant
-// C_b is accumulated alongside.
+// word are handled together: one AND per plane moves their t-bit codes into
+// the low and high 16-bit halves of one register, and a code pattern c read as
+// an fp16 is the denormal c * 2^-24 -- exact -- so one v_fma_mix_f32 per token
+// and channel adds c * (w_bj * 2^(24+4-t)) to a float32 accumulator.  That is
+// (t+2)/2 instructions per token and channel instead of one extract and one
+// multiply-add per bit.  The float32 constant C_b is accumulated alongside.
 //
 // Loads in flight bound this kernel: each channel's metadata and plane words
 // come from a ring of buffers, three to six channels deep.
@@ -51,6 +50,15 @@ __device__ __forceinline__ void load_chan(ChanData<T>& d, const uint32_t* mhead,
 // Adds one channel's contribution to the 32 scores of the lane's word.
 // q2 = qbar_j * 2^(28-t): with the fp16 scale it gives the weight of a t-bit
 // code read as an fp16 denormal (c * 2^-24).
+//
+// Token pair (i, i+16) takes its two t-bit codes from one register: the
+// codes sit at bit `pos` of the low and of the high half, pos = i for pairs
+// 0..7 and i - 8 for pairs 8..15.  Each plane word is shifted once per
+// channel into two copies (one per group of pairs) so that plane p's bit of
+// token i lands at pos + t-1-p; after that a pair costs one AND per plane and
+// two fma_mix.  A half holding c << pos (< 2^11) reads as the fp16 value
+// c * 2^(pos-24) exactly, so acc[i] collects 2^pos times its true sum; the
+// factor is removed once at the end.
 template <int T>
 __device__ __forceinline__ void use_chan(const ChanData<T>& d, float qv, float qm, float q2,
                                          float& C, float (&acc)[kTok]) {
@@ -59,14 +67,21 @@ __device__ __forceinline__ void use_chan(const ChanData<T>& d, float qv, float q
   C = __builtin_fmaf(off, qv, C);
   C = __builtin_fmaf(sc, qm, C);
   const float w = sc * q2;
+  uint32_t ua[T], ub[T];
+#pragma unroll
+  for (int p = 0; p < T; ++p) {
+    const int sft = T - 1 - p;                  // code bit of plane p
+    ua[p] = d.W[p] << sft;                       // pairs 0..7:  token i -> bit i + sft
+    ub[p] = d.W[p] >> (8 - sft);                 // pairs 8..15: token i -> bit i - 8 + sft
+  }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    uint32_t x = 0;
+    const int pos = i < 8 ? i : i - 8;
+    uint32_t x = (i < 8 ? ua[0] : ub[0]) & (0x00010001u << (pos + T - 1));
 #pragma unroll
-    for (int p = 0; p < T; ++p) {
-      const int sft = T - 1 - p;                // code bit of plane p
-      const uint32_t v = (i >= sft) ? (d.W[p] >> (i - sft)) : (d.W[p] << (sft - i));
-      x |= v & (0x00010001u << sft);           // tokens i (low half) and i+16 (high half)
+    for (int p = 1; p < T; ++p) {
+      x |= (i < 8 ? ua[p] : ub[p]) & (0x00010001u << (pos + T - 1 - p));
+      asm volatile("" : "+v"(x));               // one v_and_or_b32 per plane
     }
     asm volatile("" : "+v"(x));                 // keep x whole: its halves feed op_sel
     acc[i] = __builtin_fmaf(half_bits_to_f32(x), w, acc[i]);
@@ -196,7 +211,8 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
   float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < kTok; ++i) {
-    sv[i] = acc[i] + C;
+    const int pos = (i & 15) < 8 ? (i & 15) : (i & 15) - 8;    // acc[i] holds 2^pos x its sum
+    sv[i] = __builtin_fmaf(acc[i], __builtin_bit_cast(float, uint32_t(127 - pos) << 23), C);
     m = fmaxf(m, sv[i]);
   }
   if (valid) {
