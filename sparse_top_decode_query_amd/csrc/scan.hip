@@ -19,8 +19,12 @@
 // (t+2)/2 instructions per token and channel instead of one extract and one
 // multiply-add per bit.  The float32 constant C_b is accumulated alongside.
 //
-// Loads in flight bound this kernel: each channel's metadata and plane words
-// come from a ring of buffers, three to six channels deep.
+// Each channel's metadata and plane words come from a ring of buffers, three
+// to six channels deep, to keep loads in flight.  Scores leave through LDS:
+// lane l's 32 scores are consecutive tokens, so stores straight from the
+// lanes would scatter 16-byte pieces 128 bytes apart; staged in LDS, every
+// store instruction writes 1 KB of consecutive tokens (this alone cut the
+// kernel's time by a sixth).
 //
 // Optionally the maximum score of every 64-token block is written as well
 // (the two lanes of a block combine theirs); top-k selection uses it to skip
@@ -143,6 +147,8 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
   __shared__ float s_qm[kHeadDim];
   __shared__ int s_A;
   __shared__ int s_run[5];          // list slots where depth 4, 3, 2, 1 start; s_run[4] = A
+  // each wave's 2048 scores in token order (rows of 32 padded to 36 floats)
+  __shared__ float4 s_out[kScanWaves][64 * 9];
   const int g = blockIdx.y;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -215,11 +221,23 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
     sv[i] = __builtin_fmaf(acc[i], __builtin_bit_cast(float, uint32_t(127 - pos) << 23), C);
     m = fmaxf(m, sv[i]);
   }
-  if (valid) {
-    float4* dst = reinterpret_cast<float4*>(scores + size_t(g) * n + size_t(wd) * kTok);
+  // Scores leave through LDS so that every store instruction writes 1 KB of
+  // consecutive tokens (lane l holds tokens 32l..32l+31 of the wave's range).
+  float4* so = s_out[wave];
 #pragma unroll
-    for (int v = 0; v < kTok / 4; ++v)
-      dst[v] = make_float4(sv[4 * v], sv[4 * v + 1], sv[4 * v + 2], sv[4 * v + 3]);
+  for (int v = 0; v < kTok / 4; ++v)
+    so[lane * 9 + v] = make_float4(sv[4 * v], sv[4 * v + 1], sv[4 * v + 2], sv[4 * v + 3]);
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int wbase = (blockIdx.x * kScanWaves + wave) * 64;       // first word of the wave
+  const int nvalid = int(nw) - wbase < 64 ? int(nw) - wbase : 64; // words of the wave in range
+  float4* dst = reinterpret_cast<float4*>(scores + size_t(g) * n + size_t(wbase) * kTok);
+#pragma unroll
+  for (int v = 0; v < kTok / 4; ++v) {
+    const int f = v * 64 + lane;                                  // float4 index in the wave's range
+    const int word = f >> 3;                                      // 8 float4 per word
+    if (word < nvalid) dst[f] = so[word * 9 + (f & 7)];
   }
   if (block_max) {
     m = fmaxf(m, __shfl_xor(m, 1, 64));
