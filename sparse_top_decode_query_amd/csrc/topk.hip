@@ -449,29 +449,29 @@ __global__ __launch_bounds__(kTkThreads) void topk_final_kernel(const float* __r
 // k-th largest key (the k blocks whose maxima are >= T hold k keys >= T), so
 // every key of the exact top-k lies in a block with M_b >= T and is >= T.
 // One workgroup per row, no sorting:
-//  1. the block maxima land in LDS (asynchronous global->LDS loads);
+//  1. thread t holds the maxima of competition blocks [32t, 32t+32) in
+//     registers;
 //  2. a 4096-bin histogram of their order-preserving codes over the row's
 //     [min, max] code range locates the bin b* holding the k-th largest
 //     maximum; its lower edge is a float threshold thr <= T, so the top-k
 //     keys are among the keys >= thr;
-//  3. candidate blocks (M_b >= thr) are listed in index order;
-//  4. their keys land in LDS, up to kBmChunk blocks at a time, and the keys
-//     >= thr are listed in index order;
+//  3. candidate blocks (M_b >= thr) are listed in index order (one prefix
+//     sum over the threads, whose blocks are consecutive);
+//  4. thread t takes candidate blocks t, t + 512, ... (whole blocks: 256 B
+//     from each lane), counts its keys >= thr, and one prefix sum places
+//     them in index order;
 //  5. the exact k-th largest candidate code and its tie count are found;
 //  6. the winners are written by an index-ordered compaction (ties to the
 //     lower index), so the output comes out ascending.
-// A workgroup issues about one wave instruction per clock, so every pass is
-// kept to a handful of instructions per element (one compare per key once
-// thr is known) and the asynchronous loads keep many reads in flight without
-// unrolled code.  Rows whose candidates overflow the lists fall back to the
-// row path.  Keys must not be NaN.
-constexpr int kBmMaxBlocks = 16384;     // block maxima held in LDS (n <= 2^20)
+// The workgroup's steps are dependent latencies (a load, an LDS round trip,
+// a barrier), so each step is one pass of straight-line per-thread work.
+// Rows whose candidates overflow the lists fall back to the row path.  Keys
+// must not be NaN.
+constexpr int kBmMaxBlocks = 16384;     // n <= 2^20
+constexpr int kBmPer = kBmMaxBlocks / kTkThreads;   // block maxima per thread
 constexpr int kBmBins = 4096;
-constexpr int kBmCandBlocks = 2048;     // candidate blocks
+constexpr int kBmCandBlocks = 2048;     // candidate blocks (at most 4 per thread)
 constexpr int kBmCap = 2048;            // candidate keys
-constexpr int kBmChunk = 520;           // candidate blocks landed per round
-constexpr int kBmLand = kBmChunk * 64;  // floats: maxima + histogram, then landed blocks
-static_assert(kBmLand >= kBmMaxBlocks + kBmBins, "landing area holds the maxima and the bins");
 
 __global__ __launch_bounds__(256) void topk_block_max_kernel(const float* __restrict__ keys, int n,
                                                              int nb, float* __restrict__ bm) {
@@ -482,20 +482,6 @@ __global__ __launch_bounds__(256) void topk_block_max_kernel(const float* __rest
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
   if ((threadIdx.x & 63) == 0) bm[size_t(row) * nb + b] = v;
-}
-
-// Number of set bits of a wave mask in the lanes below this one.
-__device__ __forceinline__ int lane_rank(uint64_t m) {
-  return __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
-}
-
-// Asynchronous global->LDS loads of 4 or 16 bytes per lane; `lds` is the
-// wave-uniform base and lane l's bytes land at lds + 4 l or lds + 16 l.
-__device__ __forceinline__ void load_lds_4(const float* g, float* lds) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
-}
-__device__ __forceinline__ void load_lds_16(const float* g, float* lds) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
 // Inverse of f32_order_key on the codes of non-NaN floats (+0 for the code
@@ -515,17 +501,15 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __rest
                                                              const float* __restrict__ bm, int n,
                                                              int nb, int k, int n_sink, int n_local,
                                                              int32_t* __restrict__ out, int stride) {
-  __shared__ float land[kBmLand];
-  __shared__ int cb[kBmCandBlocks];       // candidate block numbers
+  __shared__ uint32_t sbin[kBmBins];
+  __shared__ int cb[kBmCandBlocks];       // candidate block numbers, ascending
+  __shared__ int s_cnt[640];              // kept keys per block of a chunk, then offsets
   __shared__ float ckey[kBmCap];
   __shared__ int cidx[kBmCap];
-  __shared__ int s_cnt[kBmChunk];         // kept keys per landed block, then offsets
+  __shared__ uint32_t hist[256];
   __shared__ uint32_t s_red[2 * kTkWaves];
   __shared__ int s_scan[2 * kTkWaves];
-  __shared__ int s_wsum[kTkWaves];
   __shared__ uint32_t s_thr;
-  uint32_t* sbin = reinterpret_cast<uint32_t*>(land + kBmMaxBlocks);   // after the maxima
-  uint32_t* hist = reinterpret_cast<uint32_t*>(land);                  // step 5, after landing
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int32_t* o = out + size_t(row) * stride;
   const int lo = n_sink, hi = n - n_local, m = hi - lo;
@@ -536,28 +520,37 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __rest
     topk_row<SDQ_KEY_F32_MAX>(keys, base, n, k, n_sink, n_local, o, stride);
     return;
   }
-  // 1. block maxima into LDS; loads past the row end are clamped
-  {
-    const float* brow = bm + size_t(row) * nb + blo;
-#pragma unroll 1
-    for (int j = wave; j * 64 < nbc; j += kTkWaves) {
-      const int b = j * 64 + lane;
-      load_lds_4(brow + (b < nbc ? b : nbc - 1), land + j * 64);
+  // 1. this thread's block maxima (blocks past the end read as -inf)
+  const float* brow = bm + size_t(row) * nb + blo;
+  const int b0 = tid * kBmPer;
+  float mx[kBmPer];
+  if ((reinterpret_cast<uintptr_t>(brow) & 15) == 0 && b0 + kBmPer <= nbc) {
+#pragma unroll
+    for (int u = 0; u < kBmPer; u += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(brow + b0 + u);
+      mx[u] = v.x;
+      mx[u + 1] = v.y;
+      mx[u + 2] = v.z;
+      mx[u + 3] = v.w;
     }
+  } else {
+#pragma unroll
+    for (int u = 0; u < kBmPer; ++u) mx[u] = b0 + u < nbc ? brow[b0 + u] : -INFINITY;
   }
   for (int i = tid; i < kBmBins; i += kTkThreads) sbin[i] = 0;
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  // code range of the maxima
   uint32_t cmin = 0xFFFFFFFFu, cmax = 0u;
-#pragma unroll 4
-  for (int b = tid; b < nbc; b += kTkThreads) {
-    const uint32_t c = f32_order_key(land[b]);
-    cmin = c < cmin ? c : cmin;
-    cmax = c > cmax ? c : cmax;
+#pragma unroll
+  for (int u = 0; u < kBmPer; ++u) {
+    if (b0 + u < nbc) {
+      const uint32_t cd = f32_order_key(mx[u]);
+      cmin = cd < cmin ? cd : cmin;
+      cmax = cd > cmax ? cd : cmax;
+    }
   }
 #pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) {
-    const uint32_t x = __shfl_xor(cmin, s, 64), y = __shfl_xor(cmax, s, 64);
+  for (int sft = 32; sft >= 1; sft >>= 1) {
+    const uint32_t x = __shfl_xor(cmin, sft, 64), y = __shfl_xor(cmax, sft, 64);
     cmin = x < cmin ? x : cmin;
     cmax = y > cmax ? y : cmax;
   }
@@ -576,89 +569,95 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __rest
   // bins of width 2^sh over [cmin, cmax]: (cmax - cmin) >> sh < kBmBins
   const int wbits = 32 - __clz(cmax - cmin);
   const int sh = wbits > 12 ? wbits - 12 : 0;
-  // 2. histogram of the block-maximum codes; bin b* holding the K-th largest
-#pragma unroll 4
-  for (int b = tid; b < nbc; b += kTkThreads)
-    atomicAdd(&sbin[(f32_order_key(land[b]) - cmin) >> sh], 1u);
+  // 2. histogram; bin b* holding the K-th largest maximum
+#pragma unroll
+  for (int u = 0; u < kBmPer; ++u)
+    if (b0 + u < nbc) atomicAdd(&sbin[(f32_order_key(mx[u]) - cmin) >> sh], 1u);
   __syncthreads();
   {
-    // thread t owns bins 8t..8t+7; suffix sums from the top
-    constexpr int BT = kBmBins / kTkThreads;
-    int c[BT], lsum = 0;
+    constexpr int BT = kBmBins / kTkThreads;           // bins BT*t .. BT*t+BT-1
+    int cnt[BT], lsum = 0;
 #pragma unroll
     for (int e = 0; e < BT; ++e) {
-      c[e] = sbin[BT * tid + e];
-      lsum += c[e];
+      cnt[e] = sbin[BT * tid + e];
+      lsum += cnt[e];
     }
     int tot;
     const int before = block_scan1(lsum, tot, s_scan);
     int above = tot - before - lsum;                     // maxima in higher threads' bins
 #pragma unroll
     for (int e = BT - 1; e >= 0; --e) {
-      if (above < K && above + c[e] >= K) s_thr = cmin + (uint32_t(BT * tid + e) << sh);
-      above += c[e];
+      if (above < K && above + cnt[e] >= K) s_thr = cmin + (uint32_t(BT * tid + e) << sh);
+      above += cnt[e];
     }
   }
   __syncthreads();
-  const float thr = f32_from_order_key(s_thr);   // v >= thr  <=>  bin(v) >= b*
-  // 3. candidate blocks in index order.  Wave w covers blocks
-  //    [w * BPW, (w + 1) * BPW) in rounds of 64 (lane = block); ballots give
-  //    the in-wave order.
-  constexpr int BPW = kBmMaxBlocks / kTkWaves;
+  const float thr = f32_from_order_key(s_thr);          // v >= thr  <=>  bin(v) >= b*
+  // 3. candidate blocks in index order
   uint32_t flags = 0;
-  int wcount = 0;
-#pragma unroll 4
-  for (int u = 0; u < BPW / 64; ++u) {
-    const int b = wave * BPW + u * 64 + lane;
-    const bool f = b < nbc && land[b] >= thr;
-    flags |= uint32_t(f) << u;
-    wcount += __popcll(__ballot(f));
-  }
-  if (lane == 0) s_wsum[wave] = wcount;
-  __syncthreads();
-  int ncb = 0, woff = 0;
 #pragma unroll
-  for (int w = 0; w < kTkWaves; ++w) {
-    woff += w < wave ? s_wsum[w] : 0;
-    ncb += s_wsum[w];
-  }
+  for (int u = 0; u < kBmPer; ++u) flags |= uint32_t(mx[u] >= thr) << u;   // -inf never passes
+  int ncb;
+  const int cpos = block_scan1(__popc(flags), ncb, s_scan);
   if (ncb > kBmCandBlocks) {
     topk_row<SDQ_KEY_F32_MAX>(keys, base, n, k, n_sink, n_local, o, stride);
     return;
   }
-#pragma unroll 4
-  for (int u = 0; u < BPW / 64; ++u) {
-    const bool f = (flags >> u) & 1u;
-    const uint64_t mk = __ballot(f);
-    if (f) cb[woff + lane_rank(mk)] = wave * BPW + u * 64 + lane;
-    woff += __popcll(mk);
+  {
+    int pos = cpos;
+    for (uint32_t f = flags; f; f &= f - 1) cb[pos++] = b0 + __ffs(f) - 1;
   }
   __syncthreads();
-  // 4. candidate keys in index order, kBmChunk blocks per landing round.  A
-  //    16-byte load per lane lands four blocks per wave instruction; landed
-  //    block i is then counted and written by wave i % 8: pass A counts the
-  //    keys >= thr per block, a prefix sum turns counts into offsets, pass B
-  //    writes the kept keys at offset + in-wave rank.
+  // 4. candidate keys in index order.  16 lanes share a block (lane q holds
+  //    its keys 4q..4q+3), so a wave load covers four whole blocks; a chunk
+  //    of kRC rounds x 32 blocks is in flight at once.  Per-lane counts of
+  //    keys >= thr travel four rounds to an int in 8-bit fields through the
+  //    in-group sums and prefixes; a prefix sum over the chunk's blocks
+  //    places them.
+  constexpr int kRC = 20;                               // rounds per chunk (640 blocks)
+  constexpr int kPk = kRC / 4;                          // packed counters
+  const int grp = tid >> 4, q = tid & 15;
   int nc = 0;
-#pragma unroll 1
-  for (int c0 = 0; c0 < ncb; c0 += kBmChunk) {
-    const int nch = ncb - c0 < kBmChunk ? ncb - c0 : kBmChunk;
-#pragma unroll 1
-    for (int q = wave; q * 4 < nch; q += kTkWaves) {
-      int i = q * 4 + (lane >> 4);
-      i = i < nch ? i : nch - 1;                 // clamped: the spare lanes reload a block
-      load_lds_16(keys + base + size_t(blo + cb[c0 + i]) * 64 + (lane & 15) * 4, land + q * 256);
+  for (int cc = 0; cc < ncb; cc += kRC * 32) {
+    const int nch = ncb - cc < kRC * 32 ? ncb - cc : kRC * 32;
+    float4 v[kRC];
+#pragma unroll
+    for (int r = 0; r < kRC; ++r) {
+      const int c = r * 32 + grp;                       // block within the chunk
+      const int cl = cc + (c < nch ? c : nch - 1);      // clamped: loads stay unconditional
+      v[r] = *reinterpret_cast<const float4*>(keys + base + size_t(blo + cb[cl]) * 64 + 4 * q);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-#pragma unroll 4
-    for (int i = wave; i < nch; i += kTkWaves) {
-      const int cnt = __popcll(__ballot(land[i * 64 + lane] >= thr));
-      if (lane == 0) s_cnt[i] = cnt;
+    uint32_t pk[kPk];
+#pragma unroll
+    for (int e = 0; e < kPk; ++e) pk[e] = 0;
+#pragma unroll
+    for (int r = 0; r < kRC; ++r) {
+      const uint32_t k4 = uint32_t(v[r].x >= thr) + uint32_t(v[r].y >= thr) +
+                          uint32_t(v[r].z >= thr) + uint32_t(v[r].w >= thr);
+      pk[r / 4] |= k4 << (8 * (r % 4));
+    }
+    // inclusive prefix over the 16 lanes of the group (fields never exceed 64)
+    uint32_t inc[kPk];
+#pragma unroll
+    for (int e = 0; e < kPk; ++e) {
+      uint32_t x = pk[e];
+#pragma unroll
+      for (int d = 1; d < 16; d <<= 1) {
+        const uint32_t y = __shfl_up(x, d, 16);
+        if (q >= d) x += y;
+      }
+      inc[e] = x;
+    }
+    if (q == 15) {
+#pragma unroll
+      for (int r = 0; r < kRC; ++r) {
+        const int c = r * 32 + grp;
+        if (c < nch) s_cnt[c] = int((inc[r / 4] >> (8 * (r % 4))) & 0xFFu);
+      }
     }
     __syncthreads();
     {
-      constexpr int PT = (kBmChunk + kTkThreads - 1) / kTkThreads;
+      constexpr int PT = (kRC * 32 + kTkThreads - 1) / kTkThreads;
       int cnt[PT], sum = 0;
 #pragma unroll
       for (int e = 0; e < PT; ++e) {
@@ -678,15 +677,25 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __rest
     }
     __syncthreads();
     if (nc <= kBmCap) {
-#pragma unroll 2
-      for (int i = wave; i < nch; i += kTkWaves) {
-        const float v = land[i * 64 + lane];
-        const bool f = v >= thr;
-        const uint64_t mk = __ballot(f);
-        if (f) {
-          const int pos = s_cnt[i] + lane_rank(mk);
-          ckey[pos] = v;
-          cidx[pos] = (blo + cb[c0 + i]) * 64 + lane;
+#pragma unroll
+      for (int r = 0; r < kRC; ++r) {
+        const int c = r * 32 + grp;
+        if (c < nch) {
+          const uint32_t mine = (pk[r / 4] >> (8 * (r % 4))) & 0xFFu;
+          const uint32_t before = ((inc[r / 4] >> (8 * (r % 4))) & 0xFFu) - mine;
+          if (mine) {
+            int pos = s_cnt[c] + int(before);
+            const int first = (blo + cb[cc + c]) * 64 + 4 * q;
+            const float xs[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (xs[e] >= thr) {
+                ckey[pos] = xs[e];
+                cidx[pos] = first + e;
+                ++pos;
+              }
+            }
+          }
         }
       }
     }
