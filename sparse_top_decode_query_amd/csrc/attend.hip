@@ -71,21 +71,30 @@ __global__ __launch_bounds__(kAtThreads) void attend_partial_kernel(AttendArgs a
   __syncthreads();
 
   const size_t kvbase = (size_t(r) * a.Hkv + kvh) * size_t(a.n);
+  // every K and V row of the chunk is requested before any arithmetic, so the
+  // chunk costs one memory round trip
+  constexpr int kSteps = kAtChunk / kAtRowsPerStep;
+  uint4 kw[kSteps], vw[kSteps];
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    const int t = tok[s * kAtRowsPerStep + rslot];
+    const size_t off = (kvbase + (t >= 0 ? t : 0)) * (kHeadDim / 8) + sub;
+    kw[s] = t >= 0 ? a.K[off] : make_uint4(0u, 0u, 0u, 0u);
+    vw[s] = t >= 0 ? a.V[off] : make_uint4(0u, 0u, 0u, 0u);
+  }
   // logits
-  for (int s = 0; s < kAtChunk / kAtRowsPerStep; ++s) {
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
     const int i = s * kAtRowsPerStep + rslot;
     const int t = tok[i];
+    const float kf[8] = {bf16_lo(kw[s].x), bf16_hi(kw[s].x), bf16_lo(kw[s].y), bf16_hi(kw[s].y),
+                         bf16_lo(kw[s].z), bf16_hi(kw[s].z), bf16_lo(kw[s].w), bf16_hi(kw[s].w)};
     float part[NQ];
 #pragma unroll
-    for (int h = 0; h < NQ; ++h) part[h] = 0.0f;
-    if (t >= 0) {
-      const uint4 kw = a.K[(kvbase + t) * (kHeadDim / 8) + sub];
-      const float kf[8] = {bf16_lo(kw.x), bf16_hi(kw.x), bf16_lo(kw.y), bf16_hi(kw.y),
-                           bf16_lo(kw.z), bf16_hi(kw.z), bf16_lo(kw.w), bf16_hi(kw.w)};
+    for (int h = 0; h < NQ; ++h) {
+      part[h] = 0.0f;
 #pragma unroll
-      for (int h = 0; h < NQ; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) part[h] = __builtin_fmaf(qr[h][e], kf[e], part[h]);
+      for (int e = 0; e < 8; ++e) part[h] = __builtin_fmaf(qr[h][e], kf[e], part[h]);
     }
 #pragma unroll
     for (int h = 0; h < NQ; ++h)
@@ -121,19 +130,16 @@ __global__ __launch_bounds__(kAtThreads) void attend_partial_kernel(AttendArgs a
   for (int h = 0; h < NQ; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[h][e] = 0.0f;
-  for (int s = 0; s < kAtChunk / kAtRowsPerStep; ++s) {
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
     const int i = s * kAtRowsPerStep + rslot;
-    const int t = tok[i];
-    if (t >= 0) {
-      const uint4 vw = a.V[(kvbase + t) * (kHeadDim / 8) + sub];
-      const float vf[8] = {bf16_lo(vw.x), bf16_hi(vw.x), bf16_lo(vw.y), bf16_hi(vw.y),
-                           bf16_lo(vw.z), bf16_hi(vw.z), bf16_lo(vw.w), bf16_hi(vw.w)};
+    const float vf[8] = {bf16_lo(vw[s].x), bf16_hi(vw[s].x), bf16_lo(vw[s].y), bf16_hi(vw[s].y),
+                         bf16_lo(vw[s].z), bf16_hi(vw[s].z), bf16_lo(vw[s].w), bf16_hi(vw[s].w)};
 #pragma unroll
-      for (int h = 0; h < NQ; ++h) {
-        const float p = z[i][h];
+    for (int h = 0; h < NQ; ++h) {
+      const float p = z[i][h];                  // 0 for skipped rows
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[h][e] = __builtin_fmaf(p, vf[e], o[h][e]);
-      }
+      for (int e = 0; e < 8; ++e) o[h][e] = __builtin_fmaf(p, vf[e], o[h][e]);
     }
   }
   // reduce the 4 row slots of a wave (lanes sub, sub+16, sub+32, sub+48)
@@ -168,21 +174,41 @@ __global__ __launch_bounds__(kAtThreads) void attend_partial_kernel(AttendArgs a
   }
 }
 
+// One workgroup per query head: merges the chunks' partials, kCb chunks per
+// batch with all of a batch's loads issued together.
 __global__ __launch_bounds__(kHeadDim) void attend_combine_kernel(const float* __restrict__ ws,
                                                                   int nchunks,
                                                                   float* __restrict__ out) {
+  constexpr int kCb = 16;
   const int qh = blockIdx.x, dd = threadIdx.x;
   const size_t pf = attend_partial_floats(kHeadDim);
   const float* base = ws + size_t(qh) * nchunks * pf;
   float M = -INFINITY;
-  for (int c = 0; c < nchunks; ++c) M = fmaxf(M, base[c * pf + kHeadDim]);
+  for (int c0 = 0; c0 < nchunks; c0 += kCb) {
+    float mv[kCb];
+#pragma unroll
+    for (int e = 0; e < kCb; ++e) mv[e] = c0 + e < nchunks ? base[(c0 + e) * pf + kHeadDim] : -INFINITY;
+#pragma unroll
+    for (int e = 0; e < kCb; ++e) M = fmaxf(M, mv[e]);
+  }
   float L = 0.0f, acc = 0.0f;
   if (M != -INFINITY) {
-    for (int c = 0; c < nchunks; ++c) {
-      const float m = base[c * pf + kHeadDim];
-      const float w = (m == -INFINITY) ? 0.0f : __expf(m - M);
-      L = __builtin_fmaf(base[c * pf + kHeadDim + 1], w, L);
-      acc = __builtin_fmaf(base[c * pf + dd], w, acc);
+    for (int c0 = 0; c0 < nchunks; c0 += kCb) {
+      float mv[kCb], lv[kCb], ov[kCb];
+#pragma unroll
+      for (int e = 0; e < kCb; ++e) {
+        const bool in = c0 + e < nchunks;
+        const float* pc = base + (in ? c0 + e : 0) * pf;
+        mv[e] = in ? pc[kHeadDim] : -INFINITY;
+        lv[e] = pc[kHeadDim + 1];
+        ov[e] = pc[dd];
+      }
+#pragma unroll
+      for (int e = 0; e < kCb; ++e) {
+        const float w = (mv[e] == -INFINITY) ? 0.0f : __expf(mv[e] - M);
+        L = __builtin_fmaf(lv[e], w, L);
+        acc = __builtin_fmaf(ov[e], w, acc);
+      }
     }
   }
   out[size_t(qh) * kHeadDim + dd] = (L > 0.0f) ? acc / L : 0.0f;
