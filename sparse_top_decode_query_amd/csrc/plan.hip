@@ -24,16 +24,32 @@ __global__ __launch_bounds__(64) void fathom_plan_kernel(const float* __restrict
   const int l = threadIdx.x;
   const int j0 = l, j1 = l + 64;
   const float* qg = q + size_t(g) * Hgrp * kHeadDim;
-  float a0 = qg[j0], a1 = qg[j1];
-  for (int h = 1; h < Hgrp; ++h) {
-    a0 = __fadd_rn(a0, qg[size_t(h) * kHeadDim + j0]);
-    a1 = __fadd_rn(a1, qg[size_t(h) * kHeadDim + j1]);
+  // every load is issued before the first add (one memory round trip for
+  // groups of up to kBatch heads), then the rows are summed in head order
+  constexpr int kBatch = 8;
+  const float va0 = var[size_t(g) * kHeadDim + j0], va1 = var[size_t(g) * kHeadDim + j1];
+  float a0 = 0.0f, a1 = 0.0f;
+  for (int h0 = 0; h0 < Hgrp; h0 += kBatch) {
+    float r0[kBatch], r1[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int h = h0 + k < Hgrp ? h0 + k : Hgrp - 1;
+      r0[k] = qg[size_t(h) * kHeadDim + j0];
+      r1[k] = qg[size_t(h) * kHeadDim + j1];
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {              // branch-free: rows past Hgrp are skipped
+      const bool in = h0 + k < Hgrp;
+      const float s0 = __fadd_rn(a0, r0[k]), s1 = __fadd_rn(a1, r1[k]);
+      a0 = h0 + k == 0 ? r0[k] : (in ? s0 : a0);
+      a1 = h0 + k == 0 ? r1[k] : (in ? s1 : a1);
+    }
   }
   qbar[size_t(g) * kHeadDim + j0] = a0;
   qbar[size_t(g) * kHeadDim + j1] = a1;
   // w = (qbar*qbar)*var as two rounded multiplies; -0 folded onto +0
-  const float w0 = __fadd_rn(__fmul_rn(__fmul_rn(a0, a0), var[size_t(g) * kHeadDim + j0]), 0.0f);
-  const float w1 = __fadd_rn(__fmul_rn(__fmul_rn(a1, a1), var[size_t(g) * kHeadDim + j1]), 0.0f);
+  const float w0 = __fadd_rn(__fmul_rn(__fmul_rn(a0, a0), va0), 0.0f);
+  const float w1 = __fadd_rn(__fmul_rn(__fmul_rn(a1, a1), va1), 0.0f);
 
   constexpr int NT = UNIFORM ? 1 : 4;      // candidate bits per channel
   const float step[4] = {1.0f, 0.25f, 0.0625f, 0.015625f};

@@ -289,6 +289,7 @@ def _rand_kv(g, R, Hkv, n):
 @pytest.mark.parametrize("R,Hq,Hkv,n,m,per_qh,bt", [(1, 32, 8, 4096, 512, False, 1),
                                                     (1, 32, 8, 4096, 768, True, 1),
                                                     (2, 8, 2, 1024, 10, False, 16),
+                                                    (1, 32, 8, 4096, 129, False, 16),
                                                     (1, 4, 4, 300, 300, False, 1),
                                                     (1, 8, 1, 2000, 65, False, 1)])
 def test_gather_attend_parity(sdq, R, Hq, Hkv, n, m, per_qh, bt):
