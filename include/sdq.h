@@ -168,6 +168,10 @@ int fathom_scan(const uint32_t* planes, const uint32_t* meta, const uint8_t* dep
  * is at least n - n_sink - n_local every index 0..n-1 is written and the
  * rest of the row is filled with -1.
  *   ws, ws_bytes  workspace of at least topk_select_workspace_bytes() bytes
+ *             (float32 rows: per-row histograms and candidate lists; uint8
+ *             rows of 32768 keys or more: one 256-entry histogram per 16384
+ *             keys per row; a few bytes otherwise).  Its contents on entry do
+ *             not matter and calls on one workspace must not overlap.
  * Errors: SDQ_EINVAL on null pointers, rows < 1, n < 1, k < 0, n_sink < 0,
  * n_local < 0, n_sink + n_local > n, unknown key_type, short workspace. */
 size_t topk_select_workspace_bytes(int rows, int n, int k, int key_type);

@@ -97,9 +97,7 @@ __global__ __launch_bounds__(kAtThreads) void attend_partial_kernel(AttendArgs a
       for (int e = 0; e < 8; ++e) part[h] = __builtin_fmaf(qr[h][e], kf[e], part[h]);
     }
 #pragma unroll
-    for (int h = 0; h < NQ; ++h)
-#pragma unroll
-      for (int m = 8; m >= 1; m >>= 1) part[h] += __shfl_xor(part[h], m, 64);
+    for (int h = 0; h < NQ; ++h) part[h] = row16_sum(part[h]);   // over the row's 16 lanes
     if (sub == 0) {
 #pragma unroll
       for (int h = 0; h < NQ; ++h) z[i][h] = (t >= 0) ? part[h] * a.scale : -INFINITY;

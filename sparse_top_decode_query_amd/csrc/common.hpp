@@ -71,6 +71,21 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
   return v;
 }
 
+// Sum over the 16 lanes of a DPP row (lanes 16r .. 16r+15), in every lane of
+// the row: quad swaps, then the half-row and row mirrors; no LDS traffic.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov_f32(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_mov_f32<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_mov_f32<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_mov_f32<0x141>(v);   // row_half_mirror: lane i <- lane 7-i of its half row
+  v += dpp_mov_f32<0x140>(v);   // row_mirror: lane i <- lane 15-i of its row
+  return v;
+}
+
 inline unsigned cdiv(size_t a, size_t b) { return unsigned((a + b - 1) / b); }
 
 }  // namespace sdq

@@ -6,13 +6,18 @@
 // bits, -0 first folded onto +0; uint8 distance d: 255 - d), so "best" is
 // always "largest u", and ties go to the lower index.
 //
-// Two paths:
+// Paths:
 //  * row path (one workgroup per row): MSB-first radix select (8 bits per
 //    pass, LDS histogram) finds the k-th largest code T and how many of the
 //    codes equal to T to keep; a final pass walks the row in index order and
 //    compacts the winners with block-wide prefix sums, so the output comes out
-//    ascending with no sort.  Used for short rows, uint8 keys, and as the
-//    fallback of the fast path.
+//    ascending with no sort.  Used for short float32 rows and as the fallback
+//    of the fast and block-max paths.
+//  * uint8 paths: one 256-bin histogram settles the select in a single pass
+//    (one workgroup per row), or, for long rows, per-segment histograms in
+//    the workspace let one workgroup per segment place its own winners.
+//  * block-max path (topk_select_block_max): float32 rows whose 64-key block
+//    maxima are known read only the blocks that can hold a winner.
 //  * fast path for long float32 rows (many workgroups per row): one pass
 //    builds a 2048-bin histogram of the top 11 bits of u, a tiny kernel picks
 //    the bin holding the k-th code, a second pass appends every element of
@@ -443,6 +448,355 @@ __global__ __launch_bounds__(kTkThreads) void topk_final_kernel(const float* __r
 }
 
 
+// ------------------------------------------------------------- uint8 path
+// uint8 distances, smallest first.  One workgroup per row: a 256-bin
+// histogram of the competition keys (wave-private LDS counters) gives the
+// k-th smallest value T and how many of the keys equal to T to keep (the
+// lowest-index ones); a block-wide prefix sum over the threads, whose keys
+// are consecutive, places the winners in index order.  A thread holds 256
+// keys (16-byte loads) per chunk of kU8Chunk keys; rows of one chunk are read
+// once, longer rows twice.
+constexpr int kU8PerThread = 256;
+constexpr int kU8Chunk = kU8PerThread * kTkThreads;
+
+// This thread's keys [s, s + cnt) of a chunk into w (bytes past cnt are 0).
+__device__ __forceinline__ void u8_load(const uint8_t* rowp, int s, int cnt, uint4 (&w)[16]) {
+  if (cnt == kU8PerThread && (reinterpret_cast<uintptr_t>(rowp + s) & 15) == 0) {
+    const uint4* p = reinterpret_cast<const uint4*>(rowp + s);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) w[v] = p[v];
+  } else {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      uint32_t d[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        uint32_t x = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int i = 16 * v + 4 * c + b;
+          if (i < cnt) x |= uint32_t(rowp[s + i]) << (8 * b);
+        }
+        d[c] = x;
+      }
+      w[v] = make_uint4(d[0], d[1], d[2], d[3]);
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t u8_at(const uint4 (&w)[16], int i) {
+  const uint4 v = w[i >> 4];
+  const int c = (i >> 2) & 3;
+  const uint32_t x = c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
+  return (x >> (8 * (i & 3))) & 0xFFu;
+}
+
+__global__ __launch_bounds__(kTkThreads) void topk_u8_kernel(const uint8_t* __restrict__ keys, int n,
+                                                             int k, int n_sink, int n_local,
+                                                             int32_t* __restrict__ out, int stride) {
+  __shared__ uint32_t hist[kTkWaves][256];
+  __shared__ int s_scan[2 * kTkWaves];
+  __shared__ int s_T, s_need;
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int32_t* o = out + size_t(row) * stride;
+  const int lo = n_sink, hi = n - n_local, m = hi - lo;
+  const int K = k < m ? k : m;
+  write_fixed(o, n, n_sink, n_local, K, stride);
+  if (K == m) {
+    for (int i = tid; i < m; i += kTkThreads) o[n_sink + i] = lo + i;
+    return;
+  }
+  if (K == 0) return;
+  const uint8_t* rowp = keys + size_t(row) * n;
+  for (int i = tid; i < kTkWaves * 256; i += kTkThreads) (&hist[0][0])[i] = 0;
+  __syncthreads();
+  uint4 w[16];
+  auto range = [&](int c0, int& s, int& cnt) {
+    s = c0 + tid * kU8PerThread;
+    const int e = s + kU8PerThread < hi ? s + kU8PerThread : hi;
+    cnt = e > s ? e - s : 0;
+  };
+  // 1. histogram of the distances
+  for (int c0 = lo; c0 < hi; c0 += kU8Chunk) {
+    int s, cnt;
+    range(c0, s, cnt);
+    u8_load(rowp, s, cnt, w);
+#pragma unroll
+    for (int i = 0; i < kU8PerThread; ++i)                    // unrolled: w stays in registers
+      if (i < cnt) atomicAdd(&hist[wave][u8_at(w, i)], 1u);
+  }
+  __syncthreads();
+  // 2. T = the K-th smallest distance; need = how many of its ties to keep
+  if (wave == 0) {
+    int c[4], lsum = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      int t = 0;
+#pragma unroll
+      for (int wv = 0; wv < kTkWaves; ++wv) t += int(hist[wv][4 * lane + e]);
+      c[e] = t;
+      lsum += t;
+    }
+    int inc = lsum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(inc, off, 64);
+      if (lane >= off) inc += y;
+    }
+    int below = inc - lsum;                     // keys with distance < 4 * lane
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (below < K && below + c[e] >= K) {
+        s_T = 4 * lane + e;
+        s_need = K - below;
+      }
+      below += c[e];
+    }
+  }
+  __syncthreads();
+  const uint32_t T = uint32_t(s_T);
+  const int need = s_need;
+  // 3. winners in index order: d < T, and the first `need` keys with d == T
+  int out_pos = n_sink, eq_seen = 0;
+  const bool one_chunk = m <= kU8Chunk;
+  for (int c0 = lo; c0 < hi; c0 += kU8Chunk) {
+    int s, cnt;
+    range(c0, s, cnt);
+    if (!one_chunk) u8_load(rowp, s, cnt, w);
+    // bit i of word i/32: key i of this thread has d < T (mlt) or d == T (meq)
+    uint32_t mlt[kU8PerThread / 32], meq[kU8PerThread / 32];
+#pragma unroll
+    for (int v = 0; v < kU8PerThread / 32; ++v) {
+      mlt[v] = 0;
+      meq[v] = 0;
+    }
+#pragma unroll
+    for (int i = 0; i < kU8PerThread; ++i) {
+      const uint32_t d = u8_at(w, i);
+      mlt[i / 32] |= uint32_t(i < cnt && d < T) << (i % 32);
+      meq[i / 32] |= uint32_t(i < cnt && d == T) << (i % 32);
+    }
+    int lt = 0, eq = 0;
+#pragma unroll
+    for (int v = 0; v < kU8PerThread / 32; ++v) {
+      lt += __popc(mlt[v]);
+      eq += __popc(meq[v]);
+    }
+    int elt, eeq, tlt, teq;
+    block_scan2(lt, eq, elt, eeq, tlt, teq, s_scan);
+    const int eq_left = need - eq_seen > 0 ? need - eq_seen : 0;
+    int pos = out_pos + elt + (eeq < eq_left ? eeq : eq_left);
+    int allow = eq_left - eeq;                  // ties this thread may still take
+    const int end = n_sink + K;
+#pragma unroll
+    for (int v = 0; v < kU8PerThread / 32; ++v) {
+      uint32_t e = meq[v];
+      for (; e && allow > 0; --allow) e &= e - 1;   // clear the first `allow` ties: kept
+      uint32_t win = mlt[v] | (meq[v] & ~e);
+      allow = allow > 0 ? allow : 0;
+      for (; win; win &= win - 1) {
+        if (pos < end) o[pos] = s + 32 * v + (__ffs(win) - 1);
+        ++pos;
+      }
+    }
+    out_pos += tlt + (teq < eq_left ? teq : eq_left);
+    eq_seen += teq;
+  }
+}
+
+// Many segments per row (long uint8 rows).  Pass 1: one workgroup per
+// segment of kU8Seg keys writes the segment's 256-bin histogram to the
+// workspace (LDS counters privatised per wave and lane quarter, so clustered
+// distances do not serialise on one counter).  Pass 2: one workgroup per
+// segment sums its row's histograms to find T and `need`, takes its place in
+// the row from the histograms of the segments before it, and compacts its own
+// winners in index order.  No counter is shared between workgroups.
+constexpr int kU8SegThreads = 256;
+constexpr int kU8SegPer = 64;                               // keys per thread
+constexpr int kU8Seg = kU8SegThreads * kU8SegPer;           // 16384
+
+__device__ __forceinline__ void u8_load64(const uint8_t* rowp, int s, int cnt, uint4 (&w)[4]) {
+  if (cnt == kU8SegPer && (reinterpret_cast<uintptr_t>(rowp + s) & 15) == 0) {
+    const uint4* p = reinterpret_cast<const uint4*>(rowp + s);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) w[v] = p[v];
+  } else {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      uint32_t d[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        uint32_t x = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int i = 16 * v + 4 * c + b;
+          if (i < cnt) x |= uint32_t(rowp[s + i]) << (8 * b);
+        }
+        d[c] = x;
+      }
+      w[v] = make_uint4(d[0], d[1], d[2], d[3]);
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t u8_at64(const uint4 (&w)[4], int i) {
+  const uint4 v = w[i >> 4];
+  const int c = (i >> 2) & 3;
+  const uint32_t x = c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
+  return (x >> (8 * (i & 3))) & 0xFFu;
+}
+
+__global__ __launch_bounds__(kU8SegThreads) void topk_u8_hist_kernel(const uint8_t* __restrict__ keys,
+                                                                     int n, int lo, int hi, int nseg,
+                                                                     uint32_t* __restrict__ ws) {
+  constexpr int kCopies = (kU8SegThreads / 64) * 4;         // per wave and lane quarter
+  __shared__ uint32_t h[kCopies][256];
+  const int seg = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
+  const int copy = (tid >> 6) * 4 + (tid & 3);
+  for (int i = tid; i < kCopies * 256; i += kU8SegThreads) (&h[0][0])[i] = 0;
+  const int s = lo + seg * kU8Seg + tid * kU8SegPer;
+  const int e = s + kU8SegPer < hi ? s + kU8SegPer : hi;
+  const int cnt = e > s ? e - s : 0;
+  uint4 w[4];
+  u8_load64(keys + size_t(row) * n, s, cnt, w);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kU8SegPer; ++i)
+    if (i < cnt) atomicAdd(&h[copy][u8_at64(w, i)], 1u);
+  __syncthreads();
+  uint32_t t = 0;
+#pragma unroll
+  for (int c = 0; c < kCopies; ++c) t += h[c][tid];
+  ws[(size_t(row) * nseg + seg) * 256 + tid] = t;
+}
+
+__global__ __launch_bounds__(kU8SegThreads) void topk_u8_select_kernel(
+    const uint8_t* __restrict__ keys, int n, int k, int n_sink, int n_local, int nseg,
+    const uint32_t* __restrict__ ws, int32_t* __restrict__ out, int stride) {
+  __shared__ int s_red[2 * (kU8SegThreads / 64)];
+  __shared__ int s_T, s_need;
+  const int seg = blockIdx.x, row = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int W = kU8SegThreads / 64;
+  int32_t* o = out + size_t(row) * stride;
+  const int lo = n_sink, hi = n - n_local, m = hi - lo;
+  const int K = k < m ? k : m;                               // 0 < K < m here
+  if (seg == 0) write_fixed(o, n, n_sink, n_local, K, stride);
+  // thread d: distance d's count over the row and over the segments before this one
+  const uint32_t* hr = ws + size_t(row) * nseg * 256;
+  int tot = 0, before = 0;
+  for (int s0 = 0; s0 < nseg; ++s0) {
+    const int c = int(hr[size_t(s0) * 256 + tid]);
+    tot += c;
+    if (s0 < seg) before += c;
+  }
+  // T: smallest d with (count of keys <= d) >= K; prefix over d = tid
+  int inc = tot;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(inc, off, 64);
+    if (lane >= off) inc += y;
+  }
+  if (lane == 63) s_red[wave] = inc;
+  __syncthreads();
+  int wbase = 0;
+#pragma unroll
+  for (int w = 0; w < W; ++w)
+    if (w < wave) wbase += s_red[w];
+  inc += wbase;                                              // keys with distance <= tid
+  if (inc >= K && inc - tot < K) {
+    s_T = tid;
+    s_need = K - (inc - tot);
+  }
+  __syncthreads();
+  const int T = s_T, need = s_need;
+  // keys of earlier segments with d < T, and with d == T
+  int blt = tid < T ? before : 0;
+  const int beq = (tid == T) ? before : 0;
+  __syncthreads();
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) blt += __shfl_xor(blt, off, 64);
+  int beq_w = beq;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) beq_w += __shfl_xor(beq_w, off, 64);
+  if (lane == 0) {
+    s_red[wave] = blt;
+    s_red[W + wave] = beq_w;
+  }
+  __syncthreads();
+  int lt_before = 0, eq_before = 0;
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    lt_before += s_red[w];
+    eq_before += s_red[W + w];
+  }
+  __syncthreads();
+  // this segment's keys: winners in index order
+  const int s = lo + seg * kU8Seg + tid * kU8SegPer;
+  const int e = s + kU8SegPer < hi ? s + kU8SegPer : hi;
+  const int cnt = e > s ? e - s : 0;
+  uint4 w4[4];
+  u8_load64(keys + size_t(row) * n, s, cnt, w4);
+  uint32_t mlt[2] = {0u, 0u}, meq[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < kU8SegPer; ++i) {
+    const uint32_t d = u8_at64(w4, i);
+    mlt[i / 32] |= uint32_t(i < cnt && int(d) < T) << (i % 32);
+    meq[i / 32] |= uint32_t(i < cnt && int(d) == T) << (i % 32);
+  }
+  const int lt = __popc(mlt[0]) + __popc(mlt[1]);
+  const int eq = __popc(meq[0]) + __popc(meq[1]);
+  int elt, eeq, tlt, teq;
+  {
+    // exclusive prefix over the workgroup of (lt, eq)
+    int ia = lt, ib = eq;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int x = __shfl_up(ia, off, 64), y = __shfl_up(ib, off, 64);
+      if (lane >= off) {
+        ia += x;
+        ib += y;
+      }
+    }
+    if (lane == 63) {
+      s_red[wave] = ia;
+      s_red[W + wave] = ib;
+    }
+    __syncthreads();
+    int wa = 0, wb = 0;
+    tlt = 0;
+    teq = 0;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      if (w < wave) {
+        wa += s_red[w];
+        wb += s_red[W + w];
+      }
+      tlt += s_red[w];
+      teq += s_red[W + w];
+    }
+    elt = wa + ia - lt;
+    eeq = wb + ib - eq;
+  }
+  (void)tlt;
+  (void)teq;
+  const int eq_left = need - eq_before > 0 ? need - eq_before : 0;
+  const int eq_taken_before = eq_before < need ? eq_before : need;
+  int pos = n_sink + lt_before + eq_taken_before + elt + (eeq < eq_left ? eeq : eq_left);
+  int allow = eq_left - eeq;
+  const int end = n_sink + K;
+#pragma unroll
+  for (int v = 0; v < 2; ++v) {
+    uint32_t ee = meq[v];
+    for (; ee && allow > 0; --allow) ee &= ee - 1;           // the first `allow` ties are kept
+    uint32_t win = mlt[v] | (meq[v] & ~ee);
+    allow = allow > 0 ? allow : 0;
+    for (; win; win &= win - 1) {
+      if (pos < end) o[pos] = s + 32 * v + (__ffs(win) - 1);
+      ++pos;
+    }
+  }
+}
+
 // ------------------------------------------------------------- block-max path
 // Rows whose competition range is made of whole 64-key blocks.  With M_b the
 // maximum of block b, the k-th largest block maximum T satisfies T <= the
@@ -772,9 +1126,17 @@ static bool use_block_max(int n, int n_sink, int n_local, int k, int key_type) {
          n_local % 64 == 0 && n / 64 <= kBmMaxBlocks && k < m && k <= m / 64;
 }
 
+// uint8 rows long enough to split into segments (0 < k < competition length)
+static bool use_u8_segments(int n, int n_sink, int n_local, int k) {
+  const int m = n - n_sink - n_local;
+  return m >= 2 * kU8Seg && k > 0 && k < m;
+}
+
 extern "C" size_t topk_select_workspace_bytes(int rows, int n, int k, int key_type) {
   if (rows < 1 || n < 1) return 0;
   (void)k;
+  if (key_type == SDQ_KEY_U8_MIN && n >= 2 * kU8Seg)
+    return size_t(rows) * cdiv(size_t(n), kU8Seg) * 256 * sizeof(uint32_t);
   if (key_type == SDQ_KEY_F32_MAX && n >= kFastMinComp) {
     const size_t hist = size_t(rows) * fast_ws_per_row();
     const size_t bm = size_t(rows) * size_t((n + 63) / 64) * sizeof(float);
@@ -839,12 +1201,25 @@ extern "C" int topk_select(const void* keys, int key_type, int rows, int n, int 
                        n_local, ws, idx_out, stride);
     return check_launch("topk_select");
   }
+  if (key_type == SDQ_KEY_U8_MIN && use_u8_segments(n, n_sink, n_local, k)) {
+    SDQ_REQUIRE(ws && ws_bytes >= need_ws, "topk_select: workspace of %zu bytes needed, %zu given",
+                need_ws, ws_bytes);
+    const int lo = n_sink, hi = n - n_local;
+    const int nseg = int(cdiv(size_t(hi - lo), kU8Seg));
+    const uint8_t* u8 = reinterpret_cast<const uint8_t*>(keys);
+    uint32_t* h = reinterpret_cast<uint32_t*>(ws);
+    hipLaunchKernelGGL(topk_u8_hist_kernel, dim3(nseg, rows), dim3(kU8SegThreads), 0, stream, u8, n,
+                       lo, hi, nseg, h);
+    hipLaunchKernelGGL(topk_u8_select_kernel, dim3(nseg, rows), dim3(kU8SegThreads), 0, stream, u8,
+                       n, k, n_sink, n_local, nseg, h, idx_out, stride);
+    return check_launch("topk_select");
+  }
   if (key_type == SDQ_KEY_F32_MAX)
     hipLaunchKernelGGL(topk_row_kernel<SDQ_KEY_F32_MAX>, dim3(rows), dim3(kTkThreads), 0, stream,
                        keys, n, k, n_sink, n_local, idx_out, stride);
   else
-    hipLaunchKernelGGL(topk_row_kernel<SDQ_KEY_U8_MIN>, dim3(rows), dim3(kTkThreads), 0, stream,
-                       keys, n, k, n_sink, n_local, idx_out, stride);
+    hipLaunchKernelGGL(topk_u8_kernel, dim3(rows), dim3(kTkThreads), 0, stream,
+                       reinterpret_cast<const uint8_t*>(keys), n, k, n_sink, n_local, idx_out, stride);
   return check_launch("topk_select");
 }
 

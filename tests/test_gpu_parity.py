@@ -231,12 +231,26 @@ def test_topk_block_max_degenerate(sdq):
         assert np.array_equal(host(sdq.topk_select(kt, k)), ref), k
 
 
-@pytest.mark.parametrize("rows,n,k,ns,nl", [(32, 131072, 512, 128, 128), (3, 999, 40, 0, 0),
-                                            (2, 50, 50, 0, 0), (1, 10000, 9000, 10, 10)])
-def test_topk_u8_bitexact(sdq, rows, n, k, ns, nl):
-    _say(f"topk u8 rows={rows} n={n} k={k}")
+@pytest.mark.parametrize("rows,n,k,ns,nl,dist", [(32, 131072, 512, 128, 128, "binom"),
+                                                 (3, 999, 40, 0, 0, "binom"),
+                                                 (2, 50, 50, 0, 0, "binom"),
+                                                 (1, 10000, 9000, 10, 10, "binom"),
+                                                 # segmented path: unaligned rows, a partial last
+                                                 # segment, k = 1, k = m - 1, all ties, all values
+                                                 (4, 40001, 700, 3, 5, "binom"),
+                                                 (2, 70000, 1, 0, 0, "binom"),
+                                                 (2, 65536, 65535, 0, 0, "uniform"),
+                                                 (3, 50000, 3000, 16, 0, "const"),
+                                                 (2, 100000, 5000, 0, 100, "uniform")])
+def test_topk_u8_bitexact(sdq, rows, n, k, ns, nl, dist):
+    _say(f"topk u8 rows={rows} n={n} k={k} {dist}")
     g = np.random.default_rng(7 + n)
-    keys = g.binomial(32, 0.5, size=(rows, n)).astype(np.uint8)
+    if dist == "binom":
+        keys = g.binomial(32, 0.5, size=(rows, n)).astype(np.uint8)
+    elif dist == "uniform":
+        keys = g.integers(0, 256, size=(rows, n)).astype(np.uint8)
+    else:
+        keys = np.full((rows, n), 9, np.uint8)
     got = host(sdq.topk_select(dev(keys), k, ns, nl))
     assert np.array_equal(got, _topk_ref(keys, k, ns, nl, False))
 
@@ -290,6 +304,10 @@ def _rand_kv(g, R, Hkv, n):
                                                     (1, 32, 8, 4096, 768, True, 1),
                                                     (2, 8, 2, 1024, 10, False, 16),
                                                     (1, 32, 8, 4096, 129, False, 16),
+                                                    # >= 256 index sets: one workgroup per set
+                                                    (32, 32, 8, 512, 100, False, 1),
+                                                    (8, 32, 8, 1024, 300, True, 1),
+                                                    (16, 16, 16, 512, 20, False, 16),
                                                     (1, 4, 4, 300, 300, False, 1),
                                                     (1, 8, 1, 2000, 65, False, 1)])
 def test_gather_attend_parity(sdq, R, Hq, Hkv, n, m, per_qh, bt):
