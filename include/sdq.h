@@ -221,8 +221,15 @@ int minmax_block_scan(const uint16_t* bmin, const uint16_t* bmax, const float* q
  *         distinct, and entries past the cache end are skipped as well.
  *   out   float32 [R][H_q][d]; a set with no valid entry yields zeros.
  *   ws, ws_bytes  workspace of at least gather_attend_workspace_bytes() bytes
+ *         (0 when every set fits one workgroup: then ws may be null).  It
+ *         holds the partial results of sets split over several workgroups;
+ *         its contents on entry do not matter.  Calls sharing a workspace
+ *         must not overlap.
+ * K and V must be 16-byte aligned; n < 2^23 (byte offsets within one
+ * (request, KV head) slice fit 31 bits); H_q / H_kv in {1, 2, 4, 8} when sets
+ * are shared; R * H_sel <= 65535.
  * Errors: SDQ_EINVAL on null pointers, R, H_q, H_kv, n, n_idx, block_tokens
- * < 1, H_q % H_kv != 0, d != 128, short workspace. */
+ * < 1, H_q % H_kv != 0, d != 128, the limits above, short workspace. */
 size_t gather_attend_workspace_bytes(int R, int H_q, int H_kv, int sets_per_query_head, int n_idx,
                                      int block_tokens, int d);
 int gather_attend(const float* q, const uint16_t* K, const uint16_t* V, const int32_t* idx, int R,

@@ -52,7 +52,8 @@ def test_invalid_arguments_rejected_without_launch():
     assert L.hamming_scan(p, p, 0, 10, p, s) == EINVAL
     assert L.minmax_block_scan(p, p, p, 1, 4, 0, 128, p, s) == EINVAL
     assert L.gather_attend(p, p, p, p, 1, 32, 6, 0, 100, 8, 1, 128, 1.0, p, p, 1 << 20, s) == EINVAL
-    assert L.gather_attend(p, p, p, p, 1, 32, 8, 0, 100, 8, 1, 128, 1.0, p, p, 0, s) == EINVAL
+    assert L.gather_attend(p, p, p, p, 1, 32, 8, 0, 2000, 1024, 1, 128, 1.0, p, p, 0, s) == EINVAL  # ws
+    assert L.gather_attend(p, p, p, p, 1, 32, 8, 0, 1 << 23, 512, 1, 128, 1.0, p, p, 1 << 20, s) == EINVAL
 
 
 def test_workspace_sizes():
@@ -60,5 +61,12 @@ def test_workspace_sizes():
     assert L.topk_select_workspace_bytes(8, 1 << 20, 512, 0) >= 8 * 8192 * 8
     assert L.topk_select_workspace_bytes(0, 10, 1, 0) == 0
     ws = L.gather_attend_workspace_bytes(1, 32, 8, 0, 512, 1, 128)
-    assert ws == 32 * 8 * 130 * 4          # 8 chunks of 64 rows per query head
+    # 8 sets split in 4 parts of 128 rows: a partial per query head and part
+    assert ws == 32 * 4 * 130 * 4
+    # sets of up to 128 rows take one workgroup each: no partials
+    assert L.gather_attend_workspace_bytes(1, 32, 8, 0, 128, 1, 128) == 0
+    # 512 sets of 129 16-row blocks: one workgroup per set, no partials
+    assert L.gather_attend_workspace_bytes(64, 32, 8, 0, 129, 16, 128) == 0
+    # sets longer than 4096 rows are always split
+    assert L.gather_attend_workspace_bytes(64, 32, 8, 0, 5000, 1, 128) == 64 * 32 * 2 * 130 * 4
     assert L.gather_attend_workspace_bytes(1, 32, 8, 0, 512, 1, 64) == 0

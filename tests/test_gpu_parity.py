@@ -309,7 +309,11 @@ def _rand_kv(g, R, Hkv, n):
                                                     (8, 32, 8, 1024, 300, True, 1),
                                                     (16, 16, 16, 512, 20, False, 16),
                                                     (1, 4, 4, 300, 300, False, 1),
-                                                    (1, 8, 1, 2000, 65, False, 1)])
+                                                    (1, 8, 1, 2000, 65, False, 1),
+                                                    (2, 8, 4, 700, 333, False, 1),      # 2 heads per set
+                                                    (1, 32, 4, 2048, 1000, False, 1),   # 8 heads per set
+                                                    (1, 8, 2, 999, 40, False, 3),       # 3-row blocks
+                                                    (1, 8, 2, 3000, 2900, False, 1)])   # 23 splits, ragged
 def test_gather_attend_parity(sdq, R, Hq, Hkv, n, m, per_qh, bt):
     _say(f"attend R={R} Hq={Hq} Hkv={Hkv} n={n} m={m} per_qh={per_qh} bt={bt}")
     g = np.random.default_rng(n + m)
@@ -322,6 +326,39 @@ def test_gather_attend_parity(sdq, R, Hq, Hkv, n, m, per_qh, bt):
     out = host(sdq.gather_attend(dev(q), dev(K), dev(V), dev(idx), block_tokens=bt,
                                  per_query_head=per_qh))
     ref = o_attend.attend(q, K, V, idx, block_tokens=bt, per_query_head=per_qh)
+    assert float(np.abs(out - ref).max()) <= ATTN_ATOL
+
+
+def test_gather_attend_workspace_reuse(sdq):
+    """Calls in a row on one workspace, with different split counts, stay
+    exact (each call's partials overwrite the last call's)."""
+    _say("attend workspace reuse")
+    g = np.random.default_rng(21)
+    n = 3000
+    K, V = _rand_kv(g, 1, 2, n)
+    Kd, Vd = dev(K), dev(V)
+    ws = sdq.attend_workspace(1, 8, 2, False, 2900, 1)
+    for m in (2900, 700, 2900, 129):
+        q = g.standard_normal((1, 8, 128)).astype(np.float32)
+        idx = np.stack([np.sort(g.choice(n, m, replace=False)) for _ in range(2)])[None].astype(np.int32)
+        out = host(sdq.gather_attend(dev(q), Kd, Vd, dev(idx), ws=ws))
+        ref = o_attend.attend(q, K, V, idx)
+        assert float(np.abs(out - ref).max()) <= ATTN_ATOL, m
+
+
+def test_gather_attend_blocks_past_cache_end(sdq):
+    """16-row blocks: rows of the last, partial block that lie past the cache
+    end are skipped, as are blocks wholly past it and -1 padding."""
+    _say("attend partial last block")
+    g = np.random.default_rng(11)
+    n = 1000                                   # block 62 holds rows 992..999 only
+    K, V = _rand_kv(g, 1, 1, n)
+    q = g.standard_normal((1, 4, 128)).astype(np.float32)
+    blocks = [3, 17, 40, 62, 70, -1, 5]
+    idx = np.array(blocks, np.int32)[None, None, :]
+    out = host(sdq.gather_attend(dev(q), dev(K), dev(V), dev(idx), block_tokens=16))
+    rows = [b * 16 + j for b in blocks if b >= 0 for j in range(16) if b * 16 + j < n]
+    ref = o_attend.attend(q, K, V, np.array(rows, np.int64)[None, None, :])
     assert float(np.abs(out - ref).max()) <= ATTN_ATOL
 
 
