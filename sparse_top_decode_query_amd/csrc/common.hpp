@@ -86,6 +86,47 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// DPP scans and reductions (no LDS traffic).  A DPP lane whose source lane
+// does not exist, or whose row is masked off, receives 0.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, false);
+}
+// Inclusive prefix sum within each 16-lane row.
+__device__ __forceinline__ int row16_incl_scan(int x) {
+  x += dpp_i32<0x111>(x);         // row_shr:1
+  x += dpp_i32<0x112>(x);         // row_shr:2
+  x += dpp_i32<0x114>(x);         // row_shr:4
+  x += dpp_i32<0x118>(x);         // row_shr:8
+  return x;
+}
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x = row16_incl_scan(x);
+  x += dpp_i32<0x142, 0xA>(x);    // row_bcast:15 into rows 1 and 3
+  x += dpp_i32<0x143, 0xC>(x);    // row_bcast:31 into rows 2 and 3
+  return x;
+}
+// Value of lane 63, as a wave-uniform scalar.
+__device__ __forceinline__ int wave_last(int x) { return __builtin_amdgcn_readlane(x, 63); }
+// Sum over the wave, wave-uniform.
+__device__ __forceinline__ int wave_sum_dpp(int x) { return wave_last(wave_incl_scan(x)); }
+// Min / max over the wave of unsigned values, wave-uniform: within rows by
+// DPP, then the four row results by lane reads.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_minmax_u32(uint32_t v) {
+  auto f = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+  v = f(v, uint32_t(dpp_i32<0xB1>(int(v))));     // quad_perm [1,0,3,2]
+  v = f(v, uint32_t(dpp_i32<0x4E>(int(v))));     // quad_perm [2,3,0,1]
+  v = f(v, uint32_t(dpp_i32<0x141>(int(v))));    // row_half_mirror
+  v = f(v, uint32_t(dpp_i32<0x140>(int(v))));    // row_mirror
+  const uint32_t r0 = uint32_t(__builtin_amdgcn_readlane(int(v), 0));
+  const uint32_t r1 = uint32_t(__builtin_amdgcn_readlane(int(v), 16));
+  const uint32_t r2 = uint32_t(__builtin_amdgcn_readlane(int(v), 32));
+  const uint32_t r3 = uint32_t(__builtin_amdgcn_readlane(int(v), 48));
+  return f(f(r0, r1), f(r2, r3));
+}
+
 inline unsigned cdiv(size_t a, size_t b) { return unsigned((a + b - 1) / b); }
 
 }  // namespace sdq

@@ -85,9 +85,9 @@ __device__ __forceinline__ void use_chan(const ChanData<T>& d, float qv, float q
 #pragma unroll
     for (int p = 1; p < T; ++p) {
       x |= (i < 8 ? ua[p] : ub[p]) & (0x00010001u << (pos + T - 1 - p));
-      asm volatile("" : "+v"(x));               // one v_and_or_b32 per plane
+      asm("" : "+v"(x));               // one v_and_or_b32 per plane
     }
-    asm volatile("" : "+v"(x));                 // keep x whole: its halves feed op_sel
+    asm("" : "+v"(x));                 // keep x whole: its halves feed op_sel
     acc[i] = __builtin_fmaf(half_bits_to_f32(x), w, acc[i]);
     acc[i + 16] = __builtin_fmaf(half_bits_to_f32(x >> 16), w, acc[i + 16]);
   }

@@ -58,15 +58,7 @@ __device__ __forceinline__ uint32_t load_code(const void* __restrict__ keys, siz
 __device__ __forceinline__ void block_scan2(int a, int b, int& ea, int& eb, int& ta, int& tb,
                                             int* s_scan) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int ia = a, ib = b;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int x = __shfl_up(ia, off, 64), y = __shfl_up(ib, off, 64);
-    if (lane >= off) {
-      ia += x;
-      ib += y;
-    }
-  }
+  const int ia = wave_incl_scan(a), ib = wave_incl_scan(b);
   if (lane == 63) {
     s_scan[wave] = ia;
     s_scan[kTkWaves + wave] = ib;
@@ -114,12 +106,8 @@ __device__ KthResult select_kth(int count, int K, Fetch fetch, uint32_t* hist, u
       mx = u > mx ? u : mx;
     }
   }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const uint32_t a = __shfl_xor(mn, m, 64), b = __shfl_xor(mx, m, 64);
-    mn = a < mn ? a : mn;
-    mx = b > mx ? b : mx;
-  }
+  mn = wave_minmax_u32<false>(mn);
+  mx = wave_minmax_u32<true>(mx);
   if (lane == 0) {
     s_red[wave] = mn;
     s_red[kTkWaves + wave] = mx;
@@ -148,13 +136,8 @@ __device__ KthResult select_kth(int count, int K, Fetch fetch, uint32_t* hist, u
       const int l = tid;
       const int c0 = hist[4 * l], c1 = hist[4 * l + 1], c2 = hist[4 * l + 2], c3 = hist[4 * l + 3];
       const int lsum = c0 + c1 + c2 + c3;
-      int sfx = lsum;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_down(sfx, off, 64);
-        if (l + off < 64) sfx += y;
-      }
-      const int above = sfx - lsum;
+      const int inc = wave_incl_scan(lsum);
+      const int above = wave_last(inc) - inc;           // counts in higher bins
       const int S3 = above + c3, S2 = S3 + c2, S1 = S2 + c1, S0 = S1 + c0;
       if (S3 >= need && above < need) { s_red[0] = 4 * l + 3; s_red[1] = need - above; }
       if (S2 >= need && S3 < need) { s_red[0] = 4 * l + 2; s_red[1] = need - S3; }
@@ -537,12 +520,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_u8_kernel(const uint8_t* __re
       c[e] = t;
       lsum += t;
     }
-    int inc = lsum;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(inc, off, 64);
-      if (lane >= off) inc += y;
-    }
+    const int inc = wave_incl_scan(lsum);
     int below = inc - lsum;                     // keys with distance < 4 * lane
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -690,12 +668,7 @@ __global__ __launch_bounds__(kU8SegThreads) void topk_u8_select_kernel(
     if (s0 < seg) before += c;
   }
   // T: smallest d with (count of keys <= d) >= K; prefix over d = tid
-  int inc = tot;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(inc, off, 64);
-    if (lane >= off) inc += y;
-  }
+  int inc = wave_incl_scan(tot);
   if (lane == 63) s_red[wave] = inc;
   __syncthreads();
   int wbase = 0;
@@ -713,11 +686,8 @@ __global__ __launch_bounds__(kU8SegThreads) void topk_u8_select_kernel(
   int blt = tid < T ? before : 0;
   const int beq = (tid == T) ? before : 0;
   __syncthreads();
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) blt += __shfl_xor(blt, off, 64);
-  int beq_w = beq;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) beq_w += __shfl_xor(beq_w, off, 64);
+  blt = wave_sum_dpp(blt);
+  const int beq_w = wave_sum_dpp(beq);
   if (lane == 0) {
     s_red[wave] = blt;
     s_red[W + wave] = beq_w;
@@ -748,15 +718,7 @@ __global__ __launch_bounds__(kU8SegThreads) void topk_u8_select_kernel(
   int elt, eeq, tlt, teq;
   {
     // exclusive prefix over the workgroup of (lt, eq)
-    int ia = lt, ib = eq;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int x = __shfl_up(ia, off, 64), y = __shfl_up(ib, off, 64);
-      if (lane >= off) {
-        ia += x;
-        ib += y;
-      }
-    }
+    const int ia = wave_incl_scan(lt), ib = wave_incl_scan(eq);
     if (lane == 63) {
       s_red[wave] = ia;
       s_red[W + wave] = ib;
@@ -858,8 +820,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __rest
   __shared__ uint32_t sbin[kBmBins];
   __shared__ int cb[kBmCandBlocks];       // candidate block numbers, ascending
   __shared__ int s_cnt[640];              // kept keys per block of a chunk, then offsets
-  __shared__ float ckey[kBmCap];
-  __shared__ int cidx[kBmCap];
+  __shared__ float ckey[kBmCap + 64];     // + a discard slot per lane
+  __shared__ int cidx[kBmCap + 64];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t s_red[2 * kTkWaves];
   __shared__ int s_scan[2 * kTkWaves];
@@ -902,12 +864,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __rest
       cmax = cd > cmax ? cd : cmax;
     }
   }
-#pragma unroll
-  for (int sft = 32; sft >= 1; sft >>= 1) {
-    const uint32_t x = __shfl_xor(cmin, sft, 64), y = __shfl_xor(cmax, sft, 64);
-    cmin = x < cmin ? x : cmin;
-    cmax = y > cmax ? y : cmax;
-  }
+  cmin = wave_minmax_u32<false>(cmin);
+  cmax = wave_minmax_u32<true>(cmax);
   if (lane == 0) {
     s_red[wave] = cmin;
     s_red[kTkWaves + wave] = cmax;
@@ -994,13 +952,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __rest
     uint32_t inc[kPk];
 #pragma unroll
     for (int e = 0; e < kPk; ++e) {
-      uint32_t x = pk[e];
-#pragma unroll
-      for (int d = 1; d < 16; d <<= 1) {
-        const uint32_t y = __shfl_up(x, d, 16);
-        if (q >= d) x += y;
-      }
-      inc[e] = x;
+      inc[e] = uint32_t(row16_incl_scan(int(pk[e])));
     }
     if (q == 15) {
 #pragma unroll
@@ -1031,25 +983,32 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __rest
     }
     __syncthreads();
     if (nc <= kBmCap) {
+      int offs[kRC];                                    // every offset read up front
 #pragma unroll
       for (int r = 0; r < kRC; ++r) {
         const int c = r * 32 + grp;
-        if (c < nch) {
-          const uint32_t mine = (pk[r / 4] >> (8 * (r % 4))) & 0xFFu;
-          const uint32_t before = ((inc[r / 4] >> (8 * (r % 4))) & 0xFFu) - mine;
-          if (mine) {
-            int pos = s_cnt[c] + int(before);
-            const int first = (blo + cb[cc + c]) * 64 + 4 * q;
-            const float xs[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+        offs[r] = s_cnt[c < nch ? c : nch - 1];
+      }
+      // candidates are sparse (about one per block): a round is skipped
+      // unless some lane of the wave holds one, and inside a round every lane
+      // writes its 4 keys, those below thr to its own discard slot, so no
+      // lane-divergent branch is needed
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              if (xs[e] >= thr) {
-                ckey[pos] = xs[e];
-                cidx[pos] = first + e;
-                ++pos;
-              }
-            }
-          }
+      for (int r = 0; r < kRC; ++r) {
+        const int c = r * 32 + grp;
+        const uint32_t mine = c < nch ? (pk[r / 4] >> (8 * (r % 4))) & 0xFFu : 0u;
+        if (__ballot(mine != 0) == 0) continue;         // wave-uniform
+        const uint32_t before = ((inc[r / 4] >> (8 * (r % 4))) & 0xFFu) - mine;
+        int pos = offs[r] + int(before);
+        const int first = (blo + cb[cc + (c < nch ? c : 0)]) * 64 + 4 * q;
+        const float xs[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool keep = c < nch && xs[e] >= thr;
+          const int p = keep ? pos : kBmCap + lane;
+          ckey[p] = xs[e];
+          cidx[p] = first + e;
+          pos += keep;
         }
       }
     }
