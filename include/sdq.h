@@ -157,6 +157,25 @@ int fathom_scan(const uint32_t* planes, const uint32_t* meta, const uint8_t* dep
                 const float* qbar, int G, int d, int n, float* scores, float* block_max,
                 hipStream_t stream);
 
+/* fathom_plan_scan -- fathom_plan (uniform == 0) or fathom_plan_uniform
+ * (uniform != 0) followed by fathom_scan, in one launch (Fathom summary,
+ * water-filling and bit-plane paragraphs: the plan is per query, the scan
+ * reads what the plan selects).  Every scan workgroup derives its KV head's
+ * plan with the same computation as fathom_plan, so plan and scores are
+ * identical to the two separate calls; this removes one launch and one
+ * dependent memory round trip from the decode step.
+ *   q, key_var, H_grp      as fathom_plan
+ *   budget                 budget_bits, or n_channels when uniform != 0
+ *   planes, meta, G, d, n  as fathom_scan
+ *   depth, qbar            out, or both NULL: the plan, as fathom_plan writes it
+ *   scores, block_max      as fathom_scan
+ * Errors: the union of fathom_plan's and fathom_scan's, and SDQ_EINVAL when
+ * exactly one of depth and qbar is NULL. */
+int fathom_plan_scan(const float* q, const float* key_var, int H_grp, int budget, int uniform,
+                     const uint32_t* planes, const uint32_t* meta, int G, int d, int n,
+                     uint8_t* depth, float* qbar, float* scores, float* block_max,
+                     hipStream_t stream);
+
 /* topk_select -- per-row top-k (HashAttention study notes, sec. 2.1 TOPK and
  * sec. 3.1 fixed positions; OasisKV review, per-KV-head top-K).
  *   keys      [rows][n]: float32 (SDQ_KEY_F32_MAX, largest first; must be

@@ -30,6 +30,7 @@
 // (the two lanes of a block combine theirs); top-k selection uses it to skip
 // blocks that cannot hold a winner.
 #include "common.hpp"
+#include "plan_dev.hpp"
 
 namespace sdq {
 
@@ -136,15 +137,27 @@ __device__ __forceinline__ void accum_run(int a, int end, const int* s_j, const 
     if (k < rem) use_chan<T>(ring[k], s_q[a + k], s_qm[a + k], s_q2[a + k], C, acc);
 }
 
+// Plan inputs of the fused kernel (every workgroup derives its head's plan).
+struct PlanIn {
+  const float* q;
+  const float* var;
+  int Hgrp, budget;
+  uint8_t* depth_out;     // optional copies of the plan, written by the first
+  float* qbar_out;        // workgroup of each head
+};
+
+// MODE 0: plan read from depth/qbar; 1: water-filling plan; 2: uniform plan.
+template <int MODE>
 __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
     const uint32_t* __restrict__ planes, const uint32_t* __restrict__ meta,
     const uint8_t* __restrict__ depth, const float* __restrict__ qbar, int n, int nb64,
-    float* __restrict__ scores, float* __restrict__ block_max) {
+    float* __restrict__ scores, float* __restrict__ block_max, PlanIn pin) {
   __shared__ float s_q2[kHeadDim];
   __shared__ int s_j[kHeadDim];
   __shared__ int s_t[kHeadDim];
   __shared__ float s_q[kHeadDim];
   __shared__ float s_qm[kHeadDim];
+  __shared__ float s_qbar[kHeadDim];
   __shared__ int s_A;
   __shared__ int s_run[5];          // list slots where depth 4, 3, 2, 1 start; s_run[4] = A
   // each wave's 2048 scores in token order (rows of 32 padded to 36 floats)
@@ -155,8 +168,23 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
 
   if (wave == 0) {
     // active channels sorted by depth (4 first); depths outside 1..4 are unread
-    const int t0 = depth[size_t(g) * kHeadDim + lane];
-    const int t1 = depth[size_t(g) * kHeadDim + lane + 64];
+    int t0, t1;
+    if constexpr (MODE == 0) {
+      t0 = depth[size_t(g) * kHeadDim + lane];
+      t1 = depth[size_t(g) * kHeadDim + lane + 64];
+    } else {
+      const HeadPlan p = plan_head<MODE == 2>(pin.q, pin.var, g, pin.Hgrp, pin.budget);
+      t0 = p.d0;
+      t1 = p.d1;
+      s_qbar[lane] = p.a0;
+      s_qbar[lane + 64] = p.a1;
+      if (blockIdx.x == 0 && pin.depth_out) {
+        pin.depth_out[size_t(g) * kHeadDim + lane] = uint8_t(t0);
+        pin.depth_out[size_t(g) * kHeadDim + lane + 64] = uint8_t(t1);
+        pin.qbar_out[size_t(g) * kHeadDim + lane] = p.a0;
+        pin.qbar_out[size_t(g) * kHeadDim + lane + 64] = p.a1;
+      }
+    }
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     int base = 0;
     for (int L = 4; L >= 1; --L) {
@@ -183,7 +211,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
   const int A = __builtin_amdgcn_readfirstlane(s_A);
   if (tid < A) {
     const int j = s_j[tid];
-    const float qv = qbar[size_t(g) * kHeadDim + j];
+    const float qv = MODE == 0 ? qbar[size_t(g) * kHeadDim + j] : s_qbar[j];
     const float half_gap = float((1 << (4 - s_t[tid])) - 1) * 0.5f;
     s_q[tid] = qv;
     s_qm[tid] = qv * half_gap;
@@ -249,18 +277,49 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
 
 using namespace sdq;
 
+static int scan_checks(const char* nm, const uint32_t* planes, const uint32_t* meta, int G,
+                       int d, int n, const float* scores) {
+  SDQ_REQUIRE(planes && meta && scores, "%s: null pointer", nm);
+  SDQ_REQUIRE(G >= 1, "%s: G=%d must be >= 1", nm, G);
+  SDQ_REQUIRE(n >= 64 && n % 64 == 0, "%s: n=%d must be a positive multiple of 64", nm, n);
+  SDQ_REQUIRE(d == kHeadDim, "%s: d=%d unsupported (only 128)", nm, d);
+  SDQ_REQUIRE(reinterpret_cast<uintptr_t>(scores) % 16 == 0, "%s: scores must be 16-byte aligned", nm);
+  return SDQ_OK;
+}
+
 extern "C" int fathom_scan(const uint32_t* planes, const uint32_t* meta, const uint8_t* depth,
                            const float* qbar, int G, int d, int n, float* scores, float* block_max,
                            hipStream_t stream) {
-  SDQ_REQUIRE(planes && meta && depth && qbar && scores, "fathom_scan: null pointer");
-  SDQ_REQUIRE(G >= 1, "fathom_scan: G=%d must be >= 1", G);
-  SDQ_REQUIRE(n >= 64 && n % 64 == 0, "fathom_scan: n=%d must be a positive multiple of 64", n);
-  SDQ_REQUIRE(d == kHeadDim, "fathom_scan: d=%d unsupported (only 128)", d);
-  SDQ_REQUIRE(reinterpret_cast<uintptr_t>(scores) % 16 == 0, "fathom_scan: scores must be 16-byte aligned");
+  SDQ_REQUIRE(depth && qbar, "fathom_scan: null pointer");
+  if (const int rc = scan_checks("fathom_scan", planes, meta, G, d, n, scores)) return rc;
   const int nb64 = n / 64;
   const size_t nw = size_t(n) / 32;
   dim3 grid(cdiv(nw, kScanWaves * 64), G);
-  hipLaunchKernelGGL(fathom_scan_kernel, grid, dim3(kScanWaves * 64), 0, stream, planes, meta,
-                     depth, qbar, n, nb64, scores, block_max);
+  hipLaunchKernelGGL(fathom_scan_kernel<0>, grid, dim3(kScanWaves * 64), 0, stream, planes, meta,
+                     depth, qbar, n, nb64, scores, block_max, PlanIn{});
   return check_launch("fathom_scan");
+}
+
+extern "C" int fathom_plan_scan(const float* q, const float* key_var, int H_grp, int budget,
+                                int uniform, const uint32_t* planes, const uint32_t* meta, int G,
+                                int d, int n, uint8_t* depth, float* qbar, float* scores,
+                                float* block_max, hipStream_t stream) {
+  SDQ_REQUIRE(q && key_var, "fathom_plan_scan: null pointer");
+  SDQ_REQUIRE((depth == nullptr) == (qbar == nullptr),
+              "fathom_plan_scan: depth and qbar must both be given or both be null");
+  SDQ_REQUIRE(H_grp >= 1, "fathom_plan_scan: H_grp=%d must be >= 1", H_grp);
+  SDQ_REQUIRE(budget >= 0, "fathom_plan_scan: budget/channel count %d must be >= 0", budget);
+  SDQ_REQUIRE(!uniform || budget <= d, "fathom_plan_scan: n_channels=%d exceeds d=%d", budget, d);
+  if (const int rc = scan_checks("fathom_plan_scan", planes, meta, G, d, n, scores)) return rc;
+  const int nb64 = n / 64;
+  const size_t nw = size_t(n) / 32;
+  dim3 grid(cdiv(nw, kScanWaves * 64), G);
+  const PlanIn pin{q, key_var, H_grp, budget, depth, qbar};
+  if (uniform)
+    hipLaunchKernelGGL(fathom_scan_kernel<2>, grid, dim3(kScanWaves * 64), 0, stream, planes, meta,
+                       nullptr, nullptr, n, nb64, scores, block_max, pin);
+  else
+    hipLaunchKernelGGL(fathom_scan_kernel<1>, grid, dim3(kScanWaves * 64), 0, stream, planes, meta,
+                       nullptr, nullptr, n, nb64, scores, block_max, pin);
+  return check_launch("fathom_plan_scan");
 }

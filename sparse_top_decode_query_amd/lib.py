@@ -33,6 +33,8 @@ _SIGS = {
     "fathom_plan_uniform": ([_vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp], _c_int),
     "fathom_gather": ([_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp], _c_int),
     "fathom_scan": ([_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp], _c_int),
+    "fathom_plan_scan": ([_vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp,
+                          _vp, _vp], _c_int),
     "topk_select_block_max": ([_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp], _c_int),
     "topk_select_workspace_bytes": ([_c_int, _c_int, _c_int, _c_int], _c_size),
     "topk_select": ([_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _c_size, _vp], _c_int),
@@ -195,6 +197,41 @@ def fathom_scan(index, depth, qbar, n, scores=None, block_max=None, planes=None,
                               _vp(qbar.data_ptr()), G, d, n, _vp(scores.data_ptr()), bm,
                               _stream(stream)), "fathom_scan")
     return scores
+
+
+def fathom_plan_scan(index, q, key_var, budget_bits, n, depth=None, qbar=None, scores=None,
+                     block_max=None, planes=None, meta=None, uniform_channels=None, stream=None,
+                     write_plan=True):
+    """fathom_plan (or the uniform plan with ``uniform_channels``) and fathom_scan in one
+    launch -> (depth, qbar, scores); depth/qbar are None when ``write_plan`` is False."""
+    G, d = key_var.shape
+    rows = q.shape[0]
+    if rows % G:
+        raise SDQError("q rows must be a multiple of G")
+    planes = index.planes if planes is None else planes
+    meta = index.meta if meta is None else meta
+    _dev(q, "q", 4, rows * d)
+    _dev(key_var, "key_var", 4, G * d)
+    _dev(planes, "planes", 4, G * d * 4 * (n // 32))
+    _dev(meta, "meta", 4, G * d * (n // 64))
+    if write_plan:
+        depth = _out(depth, (G, d), torch.uint8, q.device, "depth", 1)
+        qbar = _out(qbar, (G, d), torch.float32, q.device, "qbar", 4)
+        dp, qp = _vp(depth.data_ptr()), _vp(qbar.data_ptr())
+    else:
+        depth = qbar = None
+        dp = qp = _vp(0)
+    scores = _out(scores, (G, n), torch.float32, q.device, "scores", 4)
+    bm = _vp(0)
+    if block_max is not None:
+        bm = _dev(block_max, "block_max", 4, G * (n // 64))
+    uniform = uniform_channels is not None
+    budget = int(uniform_channels) if uniform else int(budget_bits)
+    _check(load().fathom_plan_scan(_vp(q.data_ptr()), _vp(key_var.data_ptr()), rows // G, budget,
+                                   int(uniform), _vp(planes.data_ptr()), _vp(meta.data_ptr()), G, d,
+                                   n, dp, qp, _vp(scores.data_ptr()), bm, _stream(stream)),
+           "fathom_plan_scan")
+    return depth, qbar, scores
 
 
 def topk_select_block_max(keys, block_max, k, n_sink=0, n_local=0, idx=None, stream=None):

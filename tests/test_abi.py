@@ -44,6 +44,9 @@ def test_invalid_arguments_rejected_without_launch():
     assert L.fathom_scan(p, p, p, p, 8, 128, 4000, p, null, s) == EINVAL    # n % 64
     assert L.fathom_scan(p, p, p, p, 8, 64, 4096, p, null, s) == EINVAL     # d != 128
     assert L.fathom_plan(p, p, 8, 4, 128, -1, p, p, s) == EINVAL             # negative budget
+    assert L.fathom_plan_scan(p, p, 4, 56, 0, p, p, 8, 128, 4096, p, null, p, null, s) == EINVAL  # depth only
+    assert L.fathom_plan_scan(p, p, 4, 56, 0, p, p, 8, 128, 4000, null, null, p, null, s) == EINVAL  # n % 64
+    assert L.fathom_plan_scan(p, p, 4, 129, 1, p, p, 8, 128, 4096, null, null, p, null, s) == EINVAL  # > d channels
     assert L.fathom_plan_uniform(p, p, 8, 4, 128, 129, p, p, s) == EINVAL    # > d channels
     assert L.fathom_ingest(p, 0, 4096, 128, p, p, s) == EINVAL               # G < 1
     assert L.topk_select(p, 7, 1, 10, 2, 0, 0, p, p, 256, s) == EINVAL       # key type

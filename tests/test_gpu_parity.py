@@ -161,6 +161,29 @@ def test_fathom_scan_uniform_and_empty_plan(sdq):
     assert np.all(got == 0) and np.all(ref == 0)
 
 
+@pytest.mark.parametrize("G,n,budget,uniform", [(8, 8192, 56, None), (2, 64 * 37, 47, None),
+                                                (3, 4096, 92, None), (2, 4096, 0, 34),
+                                                (1, 4096, 0, None), (2, 64, 512, None)])
+def test_fathom_plan_scan_fused_equals_separate(sdq, G, n, budget, uniform):
+    """The fused plan + scan gives bit-identical plan, scores and block maxima
+    to fathom_plan followed by fathom_scan (same computation, one launch)."""
+    _say(f"plan+scan fused G={G} n={n} B={budget} uniform={uniform}")
+    case = synth.fathom_case(2, n=n, heads=list(range(G)), with_values=False)
+    q, var = dev(case["q"][:G * 4]), dev(case["var"][:G])
+    index = sdq.fathom_ingest(dev(case["K"]))
+    depth, qbar = sdq.fathom_plan(q, var, budget, uniform_channels=uniform)
+    bm = torch.empty(G, n // 64, device="cuda")
+    scores = sdq.fathom_scan(index, depth, qbar, n, block_max=bm)
+    bm2 = torch.full((G, n // 64), 7.0, device="cuda")
+    d2, q2, s2 = sdq.fathom_plan_scan(index, q, var, budget, n, block_max=bm2, uniform_channels=uniform)
+    _, _, s3 = sdq.fathom_plan_scan(index, q, var, budget, n, uniform_channels=uniform, write_plan=False)
+    torch.cuda.synchronize()
+    assert torch.equal(d2, depth) and torch.equal(q2.view(torch.int32), qbar.view(torch.int32))
+    assert torch.equal(s2.view(torch.int32), scores.view(torch.int32))
+    assert torch.equal(s3.view(torch.int32), scores.view(torch.int32))
+    assert torch.equal(bm2.view(torch.int32), bm.view(torch.int32))
+
+
 # ---------------------------------------------------------------- top-k
 def _topk_ref(keys, k, n_sink, n_local, largest):
     rows = keys.shape[0]
