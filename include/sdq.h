@@ -152,7 +152,8 @@ int fathom_gather(const uint32_t* planes_host, const uint32_t* meta_host, const 
  *   scores        float32 [G][n] out
  *   block_max     float32 [G][n/64] out, or NULL: the maximum score of every
  *                 64-token block (input of topk_select_block_max)
- * Errors: SDQ_EINVAL on null pointers, G < 1, n < 64, n % 64 != 0, d != 128. */
+ * Errors: SDQ_EINVAL on null pointers, G < 1, n < 64, n % 64 != 0,
+ * n >= 2^25 (one head's planes are addressed with 31-bit offsets), d != 128. */
 int fathom_scan(const uint32_t* planes, const uint32_t* meta, const uint8_t* depth,
                 const float* qbar, int G, int d, int n, float* scores, float* block_max,
                 hipStream_t stream);

@@ -43,13 +43,23 @@ struct ChanData {
   uint32_t W[T];        // this lane's word of planes 0..T-1
 };
 
+// Where a lane's loads come from: bounds-checked buffers over the head's
+// planes and metadata, a fixed per-lane byte offset, and per-channel offsets
+// that are wave-uniform (scalar registers), so addressing costs no vector
+// instruction.
+struct ScanSrc {
+  __amdgpu_buffer_rsrc_t planes, meta;
+  uint32_t plane_off, meta_off;   // this lane's word / block, in bytes
+  uint32_t row_bytes, mrow_bytes;   // one plane row (n/8 bytes), one metadata row (n/16)
+};
+
 template <int T>
-__device__ __forceinline__ void load_chan(ChanData<T>& d, const uint32_t* mhead,
-                                          const uint32_t* phead, int j, int nb64, size_t nw) {
-  d.mw = mhead[size_t(j) * nb64];
-  const uint32_t* prow = phead + size_t(j) * 4 * nw;
+__device__ __forceinline__ void load_chan(ChanData<T>& d, const ScanSrc& src, int j) {
+  d.mw = __builtin_amdgcn_raw_buffer_load_b32(src.meta, src.meta_off, uint32_t(j) * src.mrow_bytes, 0);
+  const uint32_t base = uint32_t(j) * 4u * src.row_bytes;
 #pragma unroll
-  for (int p = 0; p < T; ++p) d.W[p] = prow[size_t(p) * nw];
+  for (int p = 0; p < T; ++p)
+    d.W[p] = __builtin_amdgcn_raw_buffer_load_b32(src.planes, src.plane_off, base + uint32_t(p) * src.row_bytes, 0);
 }
 
 // Adds one channel's contribution to the 32 scores of the lane's word.
@@ -111,13 +121,12 @@ struct RingDepth {
 template <int T>
 __device__ __forceinline__ void accum_run(int a, int end, const int* s_j, const float* s_q,
                                           const float* s_qm, const float* s_q2,
-                                          const uint32_t* mhead, const uint32_t* phead, int nb64,
-                                          size_t nw, float& C, float (&acc)[kTok]) {
+                                          const ScanSrc& src, float& C, float (&acc)[kTok]) {
   constexpr int D = RingDepth<T>::D;
   if (a >= end) return;
   auto fetch = [&](ChanData<T>& d, int x) {
     x = x < end ? x : end - 1;
-    load_chan<T>(d, mhead, phead, __builtin_amdgcn_readfirstlane(s_j[x]), nb64, nw);
+    load_chan<T>(d, src, __builtin_amdgcn_readfirstlane(s_j[x]));
   };
   ChanData<T> ring[D];
 #pragma unroll
@@ -170,8 +179,11 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
     // active channels sorted by depth (4 first); depths outside 1..4 are unread
     int t0, t1;
     if constexpr (MODE == 0) {
+      // depth and qbar in one round trip
       t0 = depth[size_t(g) * kHeadDim + lane];
       t1 = depth[size_t(g) * kHeadDim + lane + 64];
+      s_qbar[lane] = qbar[size_t(g) * kHeadDim + lane];
+      s_qbar[lane + 64] = qbar[size_t(g) * kHeadDim + lane + 64];
     } else {
       const HeadPlan p = plan_head<MODE == 2>(pin.q, pin.var, g, pin.Hgrp, pin.budget);
       t0 = p.d0;
@@ -211,7 +223,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
   const int A = __builtin_amdgcn_readfirstlane(s_A);
   if (tid < A) {
     const int j = s_j[tid];
-    const float qv = MODE == 0 ? qbar[size_t(g) * kHeadDim + j] : s_qbar[j];
+    const float qv = s_qbar[j];
     const float half_gap = float((1 << (4 - s_t[tid])) - 1) * 0.5f;
     s_q[tid] = qv;
     s_qm[tid] = qv * half_gap;
@@ -225,8 +237,16 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
   const bool valid = wd < int(nw);
   const int wdc = valid ? wd : int(nw) - 1;                       // loads stay in bounds
   const int b = wdc >> 1;
-  const uint32_t* mhead = meta + size_t(g) * kHeadDim * nb64 + b;
-  const uint32_t* phead = planes + size_t(g) * kHeadDim * 4 * nw + wdc;
+  ScanSrc src;
+  src.row_bytes = uint32_t(nw) * 4u;
+  src.mrow_bytes = uint32_t(nb64) * 4u;
+  src.planes = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(planes + size_t(g) * kHeadDim * 4 * nw), (short)0,
+      int(kHeadDim * 4 * src.row_bytes), 0x00020000);
+  src.meta = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(meta + size_t(g) * kHeadDim * nb64),
+                                               (short)0, int(kHeadDim * src.mrow_bytes), 0x00020000);
+  src.plane_off = uint32_t(wdc) * 4u;
+  src.meta_off = uint32_t(b) * 4u;
 
   // Channels are sorted by depth, so four fixed-depth runs cover them and the
   // accumulators never change registers.
@@ -236,10 +256,10 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
   for (int i = 0; i < kTok; ++i) acc[i] = 0.0f;
   const int r0 = __builtin_amdgcn_readfirstlane(s_run[0]), r1 = __builtin_amdgcn_readfirstlane(s_run[1]);
   const int r2 = __builtin_amdgcn_readfirstlane(s_run[2]), r3 = __builtin_amdgcn_readfirstlane(s_run[3]);
-  accum_run<4>(r0, r1, s_j, s_q, s_qm, s_q2, mhead, phead, nb64, nw, C, acc);
-  accum_run<3>(r1, r2, s_j, s_q, s_qm, s_q2, mhead, phead, nb64, nw, C, acc);
-  accum_run<2>(r2, r3, s_j, s_q, s_qm, s_q2, mhead, phead, nb64, nw, C, acc);
-  accum_run<1>(r3, A, s_j, s_q, s_qm, s_q2, mhead, phead, nb64, nw, C, acc);
+  accum_run<4>(r0, r1, s_j, s_q, s_qm, s_q2, src, C, acc);
+  accum_run<3>(r1, r2, s_j, s_q, s_qm, s_q2, src, C, acc);
+  accum_run<2>(r2, r3, s_j, s_q, s_qm, s_q2, src, C, acc);
+  accum_run<1>(r3, A, s_j, s_q, s_qm, s_q2, src, C, acc);
 
   float sv[kTok];
   float m = -INFINITY;
@@ -282,6 +302,7 @@ static int scan_checks(const char* nm, const uint32_t* planes, const uint32_t* m
   SDQ_REQUIRE(planes && meta && scores, "%s: null pointer", nm);
   SDQ_REQUIRE(G >= 1, "%s: G=%d must be >= 1", nm, G);
   SDQ_REQUIRE(n >= 64 && n % 64 == 0, "%s: n=%d must be a positive multiple of 64", nm, n);
+  SDQ_REQUIRE(n < (1 << 25), "%s: n=%d must be below 2^25 (a head's planes fit 2 GiB)", nm, n);
   SDQ_REQUIRE(d == kHeadDim, "%s: d=%d unsupported (only 128)", nm, d);
   SDQ_REQUIRE(reinterpret_cast<uintptr_t>(scores) % 16 == 0, "%s: scores must be 16-byte aligned", nm);
   return SDQ_OK;
