@@ -983,11 +983,12 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __rest
     }
     __syncthreads();
     if (nc <= kBmCap) {
-      int offs[kRC];                                    // every offset read up front
+      int offs[kRC], firsts[kRC];                       // every LDS read issued up front
 #pragma unroll
       for (int r = 0; r < kRC; ++r) {
         const int c = r * 32 + grp;
         offs[r] = s_cnt[c < nch ? c : nch - 1];
+        firsts[r] = (blo + cb[cc + (c < nch ? c : 0)]) * 64 + 4 * q;
       }
       // candidates are sparse (about one per block): a round is skipped
       // unless some lane of the wave holds one, and inside a round every lane
@@ -1000,7 +1001,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __rest
         if (__ballot(mine != 0) == 0) continue;         // wave-uniform
         const uint32_t before = ((inc[r / 4] >> (8 * (r % 4))) & 0xFFu) - mine;
         int pos = offs[r] + int(before);
-        const int first = (blo + cb[cc + (c < nch ? c : 0)]) * 64 + 4 * q;
+        const int first = firsts[r];
         const float xs[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
