@@ -23,7 +23,7 @@ vector ALU (one weighted accumulate per plane bit per token).
 `cpu_baseline` is the CPU oracle (fp64 NumPy) timed on the host on the same
 1M-token workload, one KV head at a time.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu] [--no-extras]
+    python bench.py [--steps K] [--warmup W] [--no-cpu] [--no-extras] [--variant hamming|minmax]
 """
 from __future__ import annotations
 
@@ -58,6 +58,9 @@ def parse_args():
                     help="skip the plan variants, the host-resident index and configs 4/5")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain 512 MiB device copies (for counter calibration)")
+    ap.add_argument("--variant", choices=("hamming", "minmax"),
+                    help="run only the config 4 (hamming) or config 5 (minmax) step, for "
+                         "kernel traces; prints one JSON line about that step")
     return ap.parse_args()
 
 
@@ -143,6 +146,9 @@ def main():
               "exchange, so the per-GPU figure is the N=1 line (run without --gpus).",
               file=sys.stderr)
         sys.exit(2)
+    if args.variant:
+        run_variant(args)
+        return
 
     import numpy as np
     import torch
@@ -351,7 +357,18 @@ def run_extras(torch, np, lib, bytemodel, synth, dev, case, K4, V4, q, var, q3, 
     log(f"extras: host gather {us:.0f} us")
     del planes_h, meta_h, stage_p, stage_m
 
-    # config 4: Hamming signatures -> top-512 + 128 sink + 128 local -> attention per query head
+    us_step, us_scan, info = variant_hamming(torch, np, lib, bytemodel, synth, dev, timeit)
+    ex["hamming_cfg4"] = info
+    log(f"extras: hamming step {us_step:.1f} us")
+    us_step, us_scan, info = variant_minmax(torch, np, lib, bytemodel, synth, dev, timeit)
+    ex["minmax_cfg5"] = info
+    log(f"extras: minmax step {us_step:.1f} us")
+    return ex
+
+
+def setup_hamming(torch, np, lib, synth, dev):
+    """Config 4: Hamming signatures -> top-512 + 128 sink + 128 local -> attention
+    per query head.  Returns (step, scan, h)."""
     h = synth.hamming_case(4)
     sigs, qsig = torch.from_numpy(h["sigs"].view(np.int32)).to(dev), torch.from_numpy(h["qsig"].view(np.int32)).to(dev)
     Kh = torch.from_numpy(h["K"].view(np.int16)).to(dev)[None]
@@ -364,20 +381,30 @@ def run_extras(torch, np, lib, bytemodel, synth, dev, case, K4, V4, q, var, q3, 
     ws_h = lib.topk_workspace(h["H"], h["n"], h["m"], lib.SDQ_KEY_U8_MIN, dev)
     ws_a = lib.attend_workspace(1, h["H"], h["Hkv"], True, m_tot, 1, dev)
 
-    def hstep(i):
+    def step(i):
         lib.hamming_scan(sigs, qsig, dist=dist)
         lib.topk_select(dist, h["m"], h["sink"], h["local"], idx=idx_h, ws=ws_h)
         lib.gather_attend(qh, Kh, Vh, idx_h[None], per_query_head=True, out=out_h, ws=ws_a)
-    us_step = timeit(torch, hstep)
-    us_scan = timeit(torch, lambda i: lib.hamming_scan(sigs, qsig, dist=dist))
-    hb = bytemodel.hamming_scan_bytes(h["n"], h["H"])
-    ex["hamming_cfg4"] = {"step_us": round(us_step, 2), "scan_us": round(us_scan, 2),
-                          "keys_scored_per_s_step": h["n"] * h["H"] / (us_step * 1e-6),
-                          "scan_hbm_frac": round(hb / (us_scan * 1e-6) / (HBM_PEAK_GBS * 1e9), 4)}
-    log(f"extras: hamming step {us_step:.1f} us")
-    del sigs, Kh, Vh, dist
 
-    # config 5: min/max block summaries, 64 requests -> top 128 blocks + local -> attention
+    def scan(i):
+        lib.hamming_scan(sigs, qsig, dist=dist)
+    return step, scan, h
+
+
+def variant_hamming(torch, np, lib, bytemodel, synth, dev, timeit):
+    step, scan, h = setup_hamming(torch, np, lib, synth, dev)
+    us_step = timeit(torch, step)
+    us_scan = timeit(torch, scan)
+    hb = bytemodel.hamming_scan_bytes(h["n"], h["H"])
+    info = {"step_us": round(us_step, 2), "scan_us": round(us_scan, 2),
+            "keys_scored_per_s_step": h["n"] * h["H"] / (us_step * 1e-6),
+            "scan_hbm_frac": round(hb / (us_scan * 1e-6) / (HBM_PEAK_GBS * 1e9), 4)}
+    return us_step, us_scan, info
+
+
+def setup_minmax(torch, np, lib, synth, dev):
+    """Config 5: min/max block summaries, 64 requests -> top 128 blocks + the
+    local block -> attention over 16-row blocks.  Returns (step, scan, mm)."""
     mm = synth.minmax_case(5)
     R, Gm, nm = mm["R"], mm["G"], mm["n"]
     Km = torch.from_numpy(mm["K"].reshape(R * Gm, nm, 128).view(np.int16)).to(dev)
@@ -394,19 +421,54 @@ def run_extras(torch, np, lib, bytemodel, synth, dev, case, K4, V4, q, var, q3, 
     qflat = qm.reshape(-1, 128)
     Kmv = Km.view(R, Gm, nm, 128)
 
-    def mstep(i):
+    def step(i):
         lib.minmax_block_scan(bmin, bmax_s, qflat, scores=S)
         lib.topk_select(S, kb, 0, 1, idx=idx_m, ws=ws_m)
         lib.gather_attend(qm, Kmv, Vm, idx_m.view(R, Gm, -1), block_tokens=16, out=out_m, ws=ws_am)
-    us_step = timeit(torch, mstep, reps=20)
-    us_scan = timeit(torch, lambda i: lib.minmax_block_scan(bmin, bmax_s, qflat, scores=S), reps=20)
+
+    def scan(i):
+        lib.minmax_block_scan(bmin, bmax_s, qflat, scores=S)
+    return step, scan, mm
+
+
+def variant_minmax(torch, np, lib, bytemodel, synth, dev, timeit):
+    step, scan, mm = setup_minmax(torch, np, lib, synth, dev)
+    R, Gm, nm, kb = mm["R"], mm["G"], mm["n"], mm["top_blocks"]
+    nbk = nm // 16
+    us_step = timeit(torch, step, reps=20)
+    us_scan = timeit(torch, scan, reps=20)
     mb = bytemodel.minmax_scan_bytes(nbk, R * Gm)
-    ex["minmax_cfg5"] = {"step_us": round(us_step, 2), "scan_us": round(us_scan, 2),
-                         "keys_scored_per_s_step": nm * R * Gm / (us_step * 1e-6),
-                         "scan_hbm_frac": round(mb / (us_scan * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
-                         "attend_bytes": bytemodel.attend_bytes((kb + 1) * 16, R * Gm)}
-    log(f"extras: minmax step {us_step:.1f} us")
-    return ex
+    info = {"step_us": round(us_step, 2), "scan_us": round(us_scan, 2),
+            "keys_scored_per_s_step": nm * R * Gm / (us_step * 1e-6),
+            "scan_hbm_frac": round(mb / (us_scan * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
+            "attend_bytes": bytemodel.attend_bytes((kb + 1) * 16, R * Gm)}
+    return us_step, us_scan, info
+
+
+def run_variant(args):
+    """--variant hamming|minmax: only that step, W warm-up + K steps, for kernel
+    traces of the variant kernels; prints one JSON line about it."""
+    import numpy as np
+    import torch
+    import synth
+    from sparse_top_decode_query_amd import lib
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    lib.load()
+    dev = torch.device("cuda:0")
+    setup = setup_hamming if args.variant == "hamming" else setup_minmax
+    step, _, _ = setup(torch, np, lib, synth, dev)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    print(json.dumps({"variant": args.variant, "steps": args.steps,
+                      "us_per_step": round(e0.elapsed_time(e1) / args.steps * 1e3, 2)}), flush=True)
 
 
 if __name__ == "__main__":
