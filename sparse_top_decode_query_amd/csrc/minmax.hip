@@ -9,7 +9,7 @@
 // -- two fused multiply-adds per dimension per block, whatever the group size.
 // The fp16 summaries feed v_fma_mix_f32 directly.  16 lanes share a block
 // (8 dimensions each, one 16-byte load of mn and one of mx), a wave covers 4
-// blocks per step; the 16 partial sums are reduced with cross-lane shuffles.
+// blocks per step; the 16 partial sums are reduced with DPP row operations.
 // HBM-bound: 512 bytes of summaries per block of 16 tokens.
 #include "common.hpp"
 
@@ -17,6 +17,7 @@ namespace sdq {
 
 constexpr int kMmThreads = 256;
 constexpr int kMmBlocksPerIter = kMmThreads / 16;   // 16 blocks per workgroup step
+constexpr int kMmIters = 8;                          // steps per workgroup
 
 __device__ __forceinline__ float fma_h(uint32_t w, int hi, float a, float acc) {
   const uint16_t bits = hi ? uint16_t(w >> 16) : uint16_t(w & 0xFFFFu);
@@ -25,7 +26,7 @@ __device__ __forceinline__ float fma_h(uint32_t w, int hi, float a, float acc) {
 
 __global__ __launch_bounds__(kMmThreads) void minmax_block_scan_kernel(
     const uint4* __restrict__ bmin, const uint4* __restrict__ bmax, const float* __restrict__ q,
-    int Hgrp, int nb, int iters, float* __restrict__ S) {
+    int Hgrp, int nb, float* __restrict__ S) {
   const int rg = blockIdx.y;
   const int tid = threadIdx.x;
   const int sub = tid & 15;             // which 8 dimensions
@@ -46,24 +47,30 @@ __global__ __launch_bounds__(kMmThreads) void minmax_block_scan_kernel(
     }
   }
   const size_t row = size_t(rg) * nb;
-  for (int it = 0; it < iters; ++it) {
-    const int b = (blockIdx.x * iters + it) * kMmBlocksPerIter + slot;
+  // every step's summaries are requested before the first is used (the
+  // index is clamped so the loads stay unconditional and in bounds)
+  uint4 lo[kMmIters], hi[kMmIters];
+#pragma unroll
+  for (int it = 0; it < kMmIters; ++it) {
+    const int b = (blockIdx.x * kMmIters + it) * kMmBlocksPerIter + slot;
+    const int bc = b < nb ? b : nb - 1;
+    lo[it] = bmin[(row + bc) * 16 + sub];
+    hi[it] = bmax[(row + bc) * 16 + sub];
+  }
+#pragma unroll
+  for (int it = 0; it < kMmIters; ++it) {
+    const int b = (blockIdx.x * kMmIters + it) * kMmBlocksPerIter + slot;
+    const uint32_t lw[4] = {lo[it].x, lo[it].y, lo[it].z, lo[it].w};
+    const uint32_t hw[4] = {hi[it].x, hi[it].y, hi[it].z, hi[it].w};
     float acc = 0.0f;
-    if (b < nb) {
-      const uint4 lo = bmin[(row + b) * 16 + sub];
-      const uint4 hi = bmax[(row + b) * 16 + sub];
-      const uint32_t lw[4] = {lo.x, lo.y, lo.z, lo.w};
-      const uint32_t hw[4] = {hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc = fma_h(hw[e], 0, P[2 * e], acc);
-        acc = fma_h(hw[e], 1, P[2 * e + 1], acc);
-        acc = fma_h(lw[e], 0, N[2 * e], acc);
-        acc = fma_h(lw[e], 1, N[2 * e + 1], acc);
-      }
+    for (int e = 0; e < 4; ++e) {
+      acc = fma_h(hw[e], 0, P[2 * e], acc);
+      acc = fma_h(hw[e], 1, P[2 * e + 1], acc);
+      acc = fma_h(lw[e], 0, N[2 * e], acc);
+      acc = fma_h(lw[e], 1, N[2 * e + 1], acc);
     }
-#pragma unroll
-    for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+    acc = row16_sum(acc);                      // the block's 16 lanes form one DPP row
     if (sub == 0 && b < nb) S[row + b] = acc;
   }
 }
@@ -81,11 +88,9 @@ extern "C" int minmax_block_scan(const uint16_t* bmin, const uint16_t* bmax, con
   SDQ_REQUIRE(d == kHeadDim, "minmax_block_scan: d=%d unsupported (only 128)", d);
   SDQ_REQUIRE(reinterpret_cast<uintptr_t>(bmin) % 16 == 0 && reinterpret_cast<uintptr_t>(bmax) % 16 == 0,
               "minmax_block_scan: summaries must be 16-byte aligned");
-  const int per_wg = 4;                                    // steps per workgroup
-  const int chunk = per_wg * kMmBlocksPerIter;
-  dim3 grid(cdiv(nb, chunk), RG);
+  dim3 grid(cdiv(nb, kMmIters * kMmBlocksPerIter), RG);
   hipLaunchKernelGGL(minmax_block_scan_kernel, grid, dim3(kMmThreads), 0, stream,
                      reinterpret_cast<const uint4*>(bmin), reinterpret_cast<const uint4*>(bmax), q,
-                     H_grp, nb, per_wg, block_scores);
+                     H_grp, nb, block_scores);
   return check_launch("minmax_block_scan");
 }
