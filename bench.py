@@ -357,6 +357,25 @@ def run_extras(torch, np, lib, bytemodel, synth, dev, case, K4, V4, q, var, q3, 
     log(f"extras: host gather {us:.0f} us")
     del planes_h, meta_h, stage_p, stage_m
 
+    # host-resident K/V rows: attention reads the k selected rows of every KV
+    # head in place over the host link (this step's own top-k output)
+    lib.topk_select_block_max(scores, bmax, k, idx=idx)
+    Kh = torch.empty(K4.shape, dtype=K4.dtype, pin_memory=True)
+    Vh = torch.empty(V4.shape, dtype=V4.dtype, pin_memory=True)
+    Kh.copy_(K4)
+    Vh.copy_(V4)
+    out = torch.empty(1, G * Hgrp, 128, device=dev)
+    ws_a = lib.attend_workspace(1, G * Hgrp, G, False, k, 1, dev)
+    torch.cuda.synchronize()
+    idx3 = idx.view(1, G, k)
+    us = timeit(torch, lambda i: lib.gather_attend_host_kv(q3, Kh, Vh, idx3, out=out, ws=ws_a), reps=10, warm=2)
+    us_dev = timeit(torch, lambda i: lib.gather_attend(q3, K4, V4, idx3, out=out, ws=ws_a), reps=10, warm=2)
+    moved = bytemodel.attend_bytes(k, G)
+    ex["offload_attend_k512"] = {"us": round(us, 1), "bytes": moved, "GB_per_s": round(moved / (us * 1e-6) / 1e9, 1),
+                                 "device_resident_us": round(us_dev, 1)}
+    log(f"extras: host K/V attention {us:.0f} us")
+    del Kh, Vh
+
     us_step, us_scan, info = variant_hamming(torch, np, lib, bytemodel, synth, dev, timeit)
     ex["hamming_cfg4"] = info
     log(f"extras: hamming step {us_step:.1f} us")

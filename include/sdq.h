@@ -257,6 +257,21 @@ int gather_attend(const float* q, const uint16_t* K, const uint16_t* V, const in
                   int d, float softmax_scale, float* out, void* ws, size_t ws_bytes,
                   hipStream_t stream);
 
+/* gather_attend_host_kv -- gather_attend with K and V left in host memory
+ * (Fathom summary, offloaded setting: the KV rows live in host memory and
+ * only the selected rows cross the host link, k * 512 bytes per set).  The
+ * kernel reads the selected rows through the buffers' device mapping; no
+ * staging copy is made.
+ *   K_host, V_host  HOST pointers to pinned, device-mapped memory, bf16
+ *                   [R][H_kv][n][d] (16-byte aligned)
+ *   everything else as gather_attend (q, idx, out and ws are device memory)
+ * Errors: as gather_attend, and SDQ_EINVAL when K_host or V_host is not
+ * pinned, device-mapped host memory. */
+int gather_attend_host_kv(const float* q, const uint16_t* K_host, const uint16_t* V_host,
+                          const int32_t* idx, int R, int H_q, int H_kv, int sets_per_query_head,
+                          int n, int n_idx, int block_tokens, int d, float softmax_scale,
+                          float* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

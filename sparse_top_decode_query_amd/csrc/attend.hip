@@ -402,28 +402,64 @@ static void launch_attend(dim3 grid, bool pow2, const AttendArgs& a, hipStream_t
     hipLaunchKernelGGL((attend_kernel<NQ, false>), grid, dim3(kAtThreads), 0, stream, a);
 }
 
+static int attend_impl(const char* nm, const float* q, const uint16_t* K, const uint16_t* V,
+                       const int32_t* idx, int R, int H_q, int H_kv, int sets_per_query_head,
+                       int n, int n_idx, int block_tokens, int d, float softmax_scale,
+                       float* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
 extern "C" int gather_attend(const float* q, const uint16_t* K, const uint16_t* V,
                              const int32_t* idx, int R, int H_q, int H_kv, int sets_per_query_head,
                              int n, int n_idx, int block_tokens, int d, float softmax_scale,
                              float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
-  SDQ_REQUIRE(q && K && V && idx && out, "gather_attend: null pointer");
+  return attend_impl("gather_attend", q, K, V, idx, R, H_q, H_kv, sets_per_query_head, n, n_idx,
+                     block_tokens, d, softmax_scale, out, ws, ws_bytes, stream);
+}
+
+// K and V stay in pinned host memory: the same kernel reads the selected rows
+// through the buffers' device mapping, over the host link.
+extern "C" int gather_attend_host_kv(const float* q, const uint16_t* K_host,
+                                     const uint16_t* V_host, const int32_t* idx, int R, int H_q,
+                                     int H_kv, int sets_per_query_head, int n, int n_idx,
+                                     int block_tokens, int d, float softmax_scale, float* out,
+                                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  SDQ_REQUIRE(K_host && V_host, "gather_attend_host_kv: null pointer");
+  void* kd = nullptr;
+  void* vd = nullptr;
+  if (hipHostGetDevicePointer(&kd, const_cast<uint16_t*>(K_host), 0) != hipSuccess || !kd ||
+      hipHostGetDevicePointer(&vd, const_cast<uint16_t*>(V_host), 0) != hipSuccess || !vd) {
+    (void)hipGetLastError();
+    set_error("gather_attend_host_kv: K and V must be pinned, device-mapped host memory");
+    return SDQ_EINVAL;
+  }
+  return attend_impl("gather_attend_host_kv", q, static_cast<const uint16_t*>(kd),
+                     static_cast<const uint16_t*>(vd), idx, R, H_q, H_kv, sets_per_query_head, n,
+                     n_idx, block_tokens, d, softmax_scale, out, ws, ws_bytes, stream);
+}
+
+static int attend_impl(const char* nm, const float* q, const uint16_t* K, const uint16_t* V,
+                       const int32_t* idx, int R, int H_q, int H_kv, int sets_per_query_head,
+                       int n, int n_idx, int block_tokens, int d, float softmax_scale,
+                       float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  SDQ_REQUIRE(q && K && V && idx && out, "%s: null pointer", nm);
   SDQ_REQUIRE(R >= 1 && H_q >= 1 && H_kv >= 1 && n >= 1 && n_idx >= 1 && block_tokens >= 1,
-              "gather_attend: R, H_q, H_kv, n, n_idx, block_tokens must be >= 1");
-  SDQ_REQUIRE(H_q % H_kv == 0, "gather_attend: H_q=%d not a multiple of H_kv=%d", H_q, H_kv);
-  SDQ_REQUIRE(d == kHeadDim, "gather_attend: d=%d unsupported (only 128)", d);
-  SDQ_REQUIRE(n < kAtMaxTokens, "gather_attend: n=%d tokens per head exceeds %d", n,
+              "%s: R, H_q, H_kv, n, n_idx, block_tokens must be >= 1", nm);
+  SDQ_REQUIRE(reinterpret_cast<uintptr_t>(K) % 16 == 0 && reinterpret_cast<uintptr_t>(V) % 16 == 0,
+              "%s: K and V must be 16-byte aligned", nm);
+  SDQ_REQUIRE(H_q % H_kv == 0, "%s: H_q=%d not a multiple of H_kv=%d", nm, H_q, H_kv);
+  SDQ_REQUIRE(d == kHeadDim, "%s: d=%d unsupported (only 128)", nm, d);
+  SDQ_REQUIRE(n < kAtMaxTokens, "%s: n=%d tokens per head exceeds %d", nm, n,
               kAtMaxTokens - 1);
-  SDQ_REQUIRE((long long)n_idx * block_tokens <= 0x7FFFFFFFLL, "gather_attend: too many rows");
+  SDQ_REQUIRE((long long)n_idx * block_tokens <= 0x7FFFFFFFLL, "%s: too many rows", nm);
   const int grp = H_q / H_kv;
   const int NQ = sets_per_query_head ? 1 : grp;
   SDQ_REQUIRE(NQ == 1 || NQ == 2 || NQ == 4 || NQ == 8,
-              "gather_attend: %d query heads per set unsupported (1, 2, 4 or 8)", NQ);
+              "%s: %d query heads per set unsupported (1, 2, 4 or 8)", nm, NQ);
   const long long sets = (long long)R * (sets_per_query_head ? H_q : H_kv);
-  SDQ_REQUIRE(sets <= 65535, "gather_attend: %lld index sets exceed 65535", sets);
+  SDQ_REQUIRE(sets <= 65535, "%s: %lld index sets exceed 65535", nm, sets);
   const size_t need = gather_attend_workspace_bytes(R, H_q, H_kv, sets_per_query_head, n_idx,
                                                     block_tokens, d);
   SDQ_REQUIRE(need == 0 || (ws && ws_bytes >= need),
-              "gather_attend: workspace of %zu bytes needed, %zu given", need, ws_bytes);
+              "%s: workspace of %zu bytes needed, %zu given", nm, need, ws_bytes);
   const long long M = (long long)n_idx * block_tokens;
   const long long per = attend_rows_per_split(sets, M);
   const long long nsplit = (M + per - 1) / per;
@@ -444,5 +480,5 @@ extern "C" int gather_attend(const float* q, const uint16_t* K, const uint16_t* 
   if (nsplit > 1)
     hipLaunchKernelGGL(attend_combine_kernel, dim3(R * H_q), dim3(kHeadDim), 0, stream,
                        reinterpret_cast<const float*>(ws), int(nsplit), out);
-  return check_launch("gather_attend");
+  return check_launch(nm);
 }

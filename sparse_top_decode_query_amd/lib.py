@@ -43,6 +43,8 @@ _SIGS = {
     "gather_attend_workspace_bytes": ([_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int], _c_size),
     "gather_attend": ([_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                        _c_int, _f, _vp, _vp, _c_size, _vp], _c_int),
+    "gather_attend_host_kv": ([_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                       _c_int, _f, _vp, _vp, _c_size, _vp], _c_int),
 }
 
 
@@ -306,6 +308,34 @@ def attend_workspace(R, Hq, Hkv, per_query_head, n_idx, block_tokens, device="cu
     nbytes = int(load().gather_attend_workspace_bytes(R, Hq, Hkv, int(per_query_head), n_idx,
                                                       block_tokens, D))
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def gather_attend_host_kv(q, K_host, V_host, idx, block_tokens=1, per_query_head=False,
+                          softmax_scale=None, out=None, ws=None, stream=None):
+    """As gather_attend, with K and V pinned host tensors (bf16 bits as int16/uint16)
+    read in place over the host link."""
+    R, Hq, d = q.shape
+    _, Hkv, n, _ = K_host.shape
+    n_idx = idx.shape[-1]
+    Hsel = Hq if per_query_head else Hkv
+    for t, nm in ((K_host, "K_host"), (V_host, "V_host")):
+        if t.is_cuda or not t.is_pinned() or not t.is_contiguous() or t.element_size() != 2:
+            raise SDQError(f"{nm} must be a contiguous pinned host tensor of 2-byte elements")
+        if t.numel() != R * Hkv * n * d:
+            raise SDQError(f"{nm} has the wrong size")
+    _dev(q, "q", 4, R * Hq * d)
+    _dev(idx, "idx", 4, R * Hsel * n_idx)
+    out = _out(out, (R, Hq, d), torch.float32, q.device, "out", 4)
+    if ws is None:
+        ws = attend_workspace(R, Hq, Hkv, per_query_head, n_idx, block_tokens, q.device)
+    _dev(ws, "ws", 1)
+    scale = (1.0 / d ** 0.5) if softmax_scale is None else float(softmax_scale)
+    _check(load().gather_attend_host_kv(_vp(q.data_ptr()), _vp(K_host.data_ptr()),
+                                        _vp(V_host.data_ptr()), _vp(idx.data_ptr()), R, Hq, Hkv,
+                                        int(bool(per_query_head)), n, n_idx, int(block_tokens), d,
+                                        scale, _vp(out.data_ptr()), _vp(ws.data_ptr()), ws.numel(),
+                                        _stream(stream)), "gather_attend_host_kv")
+    return out
 
 
 def gather_attend(q, K, V, idx, block_tokens=1, per_query_head=False, softmax_scale=None,

@@ -369,6 +369,31 @@ def test_gather_attend_workspace_reuse(sdq):
         assert float(np.abs(out - ref).max()) <= ATTN_ATOL, m
 
 
+@pytest.mark.parametrize("R,Hq,Hkv,n,m,per_qh,bt", [(1, 32, 8, 8192, 512, False, 1),
+                                                    (2, 8, 2, 4096, 40, False, 16),
+                                                    (1, 8, 8, 3000, 300, True, 1)])
+def test_gather_attend_host_kv_equals_device(sdq, R, Hq, Hkv, n, m, per_qh, bt):
+    """K and V in pinned host memory, read in place over the host link: the
+    same result as the device-resident call, and within tolerance of the
+    oracle."""
+    _say(f"attend host K/V R={R} Hq={Hq} Hkv={Hkv} n={n} m={m} per_qh={per_qh} bt={bt}")
+    g = np.random.default_rng(77 + n)
+    K, V = _rand_kv(g, R, Hkv, n)
+    q = g.standard_normal((R, Hq, 128)).astype(np.float32)
+    Hsel = Hq if per_qh else Hkv
+    idx = np.stack([np.stack([np.sort(g.choice(n // bt, m, replace=False)) for _ in range(Hsel)])
+                    for _ in range(R)]).astype(np.int32)
+    Kh = torch.from_numpy(K.view(np.int16)).pin_memory()
+    Vh = torch.from_numpy(V.view(np.int16)).pin_memory()
+    out_h = host(sdq.gather_attend_host_kv(dev(q), Kh, Vh, dev(idx), block_tokens=bt, per_query_head=per_qh))
+    out_d = host(sdq.gather_attend(dev(q), dev(K), dev(V), dev(idx), block_tokens=bt, per_query_head=per_qh))
+    assert np.array_equal(out_h.view(np.uint32), out_d.view(np.uint32))
+    ref = o_attend.attend(q, K, V, idx, block_tokens=bt, per_query_head=per_qh)
+    assert float(np.abs(out_h - ref).max()) <= ATTN_ATOL
+    with pytest.raises(sdq.SDQError):                       # device tensors are refused
+        sdq.gather_attend_host_kv(dev(q), dev(K), dev(V), dev(idx))
+
+
 def test_gather_attend_blocks_past_cache_end(sdq):
     """16-row blocks: rows of the last, partial block that lie past the cache
     end are skipped, as are blocks wholly past it and -1 padding."""
