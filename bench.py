@@ -396,6 +396,14 @@ def run_extras(torch, np, lib, bytemodel, synth, dev, case, K4, V4, q, var, q3, 
     log(f"extras: host K/V attention {us:.0f} us")
     del Kh, Vh
 
+    # read-plan quality on this layer: sparse vs dense attention error, needle and
+    # exact top-k recall, scan bytes per plan
+    from sparse_top_decode_query_amd import quality
+    t0 = time.time()
+    ex["quality_1M"] = quality.evaluate(K4[0], V4[0], q, var, index, case["needle_pos"], k)
+    log(f"extras: plan quality in {time.time() - t0:.1f} s")
+    torch.cuda.empty_cache()
+
     us_step, us_scan, info = variant_hamming(torch, np, lib, bytemodel, synth, dev, timeit)
     ex["hamming_cfg4"] = info
     log(f"extras: hamming step {us_step:.1f} us")
