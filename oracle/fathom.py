@@ -26,11 +26,16 @@ Readings taken where the page is silent:
     (gain descending, channel ascending, bit ascending);
   * the budget counts plane bits only (metadata is separate).
 
-Layouts (shared with the GPU path by definition, not by code):
-  planes  uint32 [d][4][n/32]  plane p holds code bit (3-p) (p=0 is the MSB);
-                               token i is bit (i & 31) of word (i >> 5)
-  meta    uint32 [d][n/64]     low half = fp16 scale bits, high half = fp16
-                               offset bits, one word per 64-token block
+  * a growing cache's last, partly filled block is quantised over the
+    tokens it holds (its scale and offset change as tokens arrive) and its
+    absent tokens hold code 0; a block is final once its 64 tokens are in.
+
+Layouts (shared with the GPU path by definition, not by code), for a row
+capacity of n_cap tokens (a multiple of 64; n_cap = n for a full index):
+  planes  uint32 [d][4][n_cap/32]  plane p holds code bit (3-p) (p=0 is the
+                                   MSB); token i is bit (i & 31) of word (i >> 5)
+  meta    uint32 [d][n_cap/64]     low half = fp16 scale bits, high half =
+                                   fp16 offset bits, one word per 64-token block
 """
 from __future__ import annotations
 
@@ -47,36 +52,56 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------
 # quantiser and plane packing (one KV head)
 # --------------------------------------------------------------------------
+def quantise_block(x: np.ndarray):
+    """One 64-token block of one head: float32 keys [m][...] of the m >= 1
+    tokens present -> codes uint8 [m][...], scale and offset float16 [...]
+    (any trailing shape: channels, or blocks x channels)."""
+    mn = x.min(axis=0)
+    mx = x.max(axis=0)
+    offset = mn.astype(np.float16)
+    scale = ((mx - mn) / np.float32(15.0)).astype(np.float32).astype(np.float16)
+    off32 = offset.astype(np.float32)[None]
+    sc32 = scale.astype(np.float32)[None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.rint((x - off32) / sc32)
+    r = np.where(sc32 == 0, np.float32(0), r)
+    return np.clip(r, 0, 15).astype(np.uint8), scale, offset
+
+
 def quantise(k_bf16: np.ndarray):
     """4-bit per-channel block quantiser of one head's keys.
 
-    k_bf16: uint16 [n][d] (bf16 bits), n a multiple of 64.
-    Returns codes uint8 [n][d], scale float16 [nb][d], offset float16 [nb][d].
+    k_bf16: uint16 [n][d] (bf16 bits), any n >= 1.  Every 64-token block is
+    quantised over the tokens it holds: a last, partly filled block (the open
+    block of a growing cache) takes its scale and offset from its present
+    tokens only, and is quantised again as tokens arrive until it is full.
+    Returns codes uint8 [n][d], scale float16 [nb][d], offset float16 [nb][d]
+    with nb = ceil(n / 64).
     """
     x = bf16_bits_to_f32(k_bf16)
     n, d = x.shape
-    assert n % BLOCK == 0
-    nb = n // BLOCK
-    xb = x.reshape(nb, BLOCK, d)
-    mn = xb.min(axis=1)
-    mx = xb.max(axis=1)
-    offset = mn.astype(np.float16)
-    scale = ((mx - mn) / np.float32(15.0)).astype(np.float32).astype(np.float16)
-    off32 = offset.astype(np.float32)[:, None, :]
-    sc32 = scale.astype(np.float32)[:, None, :]
-    with np.errstate(divide="ignore", invalid="ignore"):
-        r = np.rint((xb - off32) / sc32)
-    r = np.where(sc32 == 0, np.float32(0), r)
-    codes = np.clip(r, 0, 15).astype(np.uint8).reshape(n, d)
+    nf = n // BLOCK                       # full blocks, quantised side by side
+    codes = np.zeros((n, d), np.uint8)
+    scale = np.zeros((-(-n // BLOCK), d), np.float16)
+    offset = np.zeros_like(scale)
+    if nf:
+        c, sc, off = quantise_block(x[:nf * BLOCK].reshape(nf, BLOCK, d).transpose(1, 0, 2))
+        codes[:nf * BLOCK] = c.transpose(1, 0, 2).reshape(nf * BLOCK, d)
+        scale[:nf], offset[:nf] = sc, off
+    if n > nf * BLOCK:
+        codes[nf * BLOCK:], scale[nf], offset[nf] = quantise_block(x[nf * BLOCK:])
     return codes, scale, offset
 
 
-def pack_planes(codes: np.ndarray) -> np.ndarray:
-    """codes uint8 [n][d] -> planes uint32 [d][4][n/32]."""
+def pack_planes(codes: np.ndarray, n_cap: int | None = None) -> np.ndarray:
+    """codes uint8 [n][d] -> planes uint32 [d][4][n_cap/32]; tokens from n
+    up to the row capacity n_cap (default: n rounded up to 64) hold 0 bits."""
     n, d = codes.shape
-    assert n % 32 == 0
-    planes = np.zeros((d, BITS, n // 32), np.uint32)
-    ct = np.ascontiguousarray(codes.T)                                  # [d][n]
+    n_cap = -(-n // BLOCK) * BLOCK if n_cap is None else int(n_cap)
+    assert n_cap % BLOCK == 0 and n_cap >= n
+    planes = np.zeros((d, BITS, n_cap // 32), np.uint32)
+    ct = np.zeros((d, n_cap), np.uint8)
+    ct[:, :n] = codes.T                                                 # [d][n_cap]
     for p in range(BITS):
         bits = (ct >> (BITS - 1 - p)) & 1                               # [d][n]
         # byte b of a channel's bit string holds tokens 8b..8b+7, token 8b in bit 0;
@@ -86,11 +111,16 @@ def pack_planes(codes: np.ndarray) -> np.ndarray:
     return planes
 
 
-def pack_meta(scale: np.ndarray, offset: np.ndarray) -> np.ndarray:
-    """scale/offset float16 [nb][d] -> meta uint32 [d][nb]."""
+def pack_meta(scale: np.ndarray, offset: np.ndarray, nb_cap: int | None = None) -> np.ndarray:
+    """scale/offset float16 [nb][d] -> meta uint32 [d][nb_cap] (blocks past
+    nb hold 0)."""
     s = scale.view(np.uint16).astype(np.uint32)
     o = offset.view(np.uint16).astype(np.uint32)
-    return np.ascontiguousarray((s | (o << 16)).T)
+    nb, d = s.shape
+    nb_cap = nb if nb_cap is None else int(nb_cap)
+    meta = np.zeros((d, nb_cap), np.uint32)
+    meta[:, :nb] = (s | (o << 16)).T
+    return meta
 
 
 def unpack_meta(meta: np.ndarray):
@@ -114,13 +144,22 @@ def prefix_code(planes_j: np.ndarray, t: int, n: int) -> np.ndarray:
     return c
 
 
-def ingest(k_bf16_heads: np.ndarray):
-    """All heads: uint16 [G][n][d] -> planes uint32 [G][d][4][n/32], meta uint32 [G][d][n/64]."""
+def ingest(k_bf16_heads: np.ndarray, n: int | None = None, n_cap: int | None = None):
+    """Index of the first n tokens of every head (default: all of them).
+
+    k_bf16_heads uint16 [G][>=n][d] -> planes uint32 [G][d][4][n_cap/32],
+    meta uint32 [G][d][n_cap/64]; n_cap defaults to n rounded up to 64.  The
+    result is what a growing index holds once its first n tokens have been
+    appended, however the appends were split: closed blocks are final, the
+    open block is quantised over its present tokens, and everything past
+    token n is zero here (left as it was by the GPU append)."""
+    n = k_bf16_heads.shape[1] if n is None else int(n)
+    n_cap = -(-n // BLOCK) * BLOCK if n_cap is None else int(n_cap)
     planes, metas = [], []
     for kh in k_bf16_heads:
-        codes, scale, offset = quantise(kh)
-        planes.append(pack_planes(codes))
-        metas.append(pack_meta(scale, offset))
+        codes, scale, offset = quantise(kh[:n])
+        planes.append(pack_planes(codes, n_cap))
+        metas.append(pack_meta(scale, offset, n_cap // BLOCK))
     return np.stack(planes), np.stack(metas)
 
 

@@ -21,13 +21,13 @@ def bf16_bits_to_f32(b):
 
 
 def summaries(k_bf16: np.ndarray, block: int = 16):
-    """k_bf16 uint16 [n][d] -> (mn, mx) float16 [nb][d], nb = n / block."""
+    """k_bf16 uint16 [n][d] -> (mn, mx) float16 [nb][d], nb = ceil(n / block).
+    A last, partly filled block is summarised over the tokens it holds."""
     x = bf16_bits_to_f32(k_bf16)
     n, d = x.shape
-    assert n % block == 0
-    xb = x.reshape(n // block, block, d)
-    lo = xb.min(axis=1)
-    hi = xb.max(axis=1)
+    nb = -(-n // block)
+    lo = np.stack([x[b * block:min(n, (b + 1) * block)].min(axis=0) for b in range(nb)])
+    hi = np.stack([x[b * block:min(n, (b + 1) * block)].max(axis=0) for b in range(nb)])
     mn = lo.astype(np.float16)
     mx = hi.astype(np.float16)
     mn = np.where(mn.astype(np.float32) > lo, np.nextafter(mn, np.float16(-np.inf)), mn)

@@ -165,6 +165,67 @@ def test_pack_unpack_roundtrip_and_prefix():
     assert np.array_equal(o.T.view(np.uint16), offset.view(np.uint16))
 
 
+def test_open_block_is_quantised_over_its_present_tokens():
+    """A block holding m < 64 tokens quantises like the full block in which
+    the 64 - m absent tokens repeat a present key (min and max unchanged);
+    absent tokens hold code 0 in the planes, and the reconstruction bound of
+    the full quantiser holds for every present key."""
+    d = 16
+    for n in (1, 5, 63, 64 + 17, 128 + 63):
+        k = _keys(n, d, 20 + n)
+        codes, scale, offset = fathom.quantise(k)
+        assert codes.shape == (n, d) and scale.shape == (-(-n // 64), d)
+        m = n % 64 or 64
+        pad = np.concatenate([k[n - m:], np.repeat(k[n - 1:n], 64 - m, axis=0)])
+        c_full, s_full, o_full = fathom.quantise(pad)
+        assert np.array_equal(codes[n - m:], c_full[:m])
+        assert np.array_equal(scale[-1].view(np.uint16), s_full[0].view(np.uint16))
+        assert np.array_equal(offset[-1].view(np.uint16), o_full[0].view(np.uint16))
+        x = fathom.bf16_bits_to_f32(k[n - m:]).astype(np.float64)
+        sc, off = scale[-1].astype(np.float64), offset[-1].astype(np.float64)
+        err = np.abs(off + sc * codes[n - m:] - x)
+        assert np.all(err <= sc / 2 + np.abs(off) * 2 ** -11 + 16 * sc * 2 ** -11 + 1e-12)
+        pl = fathom.pack_planes(codes)
+        assert pl.shape == (d, 4, -(-n // 64) * 2)
+        for j in range(d):
+            for p in range(4):
+                assert fathom.plane_bits(pl[j], p, pl.shape[2] * 32)[n:].sum() == 0
+
+
+def test_growing_index_closed_blocks_are_final():
+    """The index of a prefix agrees with the index of any longer prefix on
+    every block that is full in both; the open block changes until full; a
+    capacity layout is the same rows with zero words appended."""
+    G, d, n_cap = 2, 8, 320
+    k = np.stack([_keys(n_cap, d, 40 + g) for g in range(G)])
+    full_p, full_m = fathom.ingest(k, n_cap, n_cap)
+    for n in (1, 63, 64, 65, 130, 200, 256, 319):
+        p, m = fathom.ingest(k, n, n_cap)
+        assert p.shape == full_p.shape and m.shape == full_m.shape
+        nf = n // 64
+        assert np.array_equal(p[..., :nf * 2], full_p[..., :nf * 2])
+        assert np.array_equal(m[..., :nf], full_m[..., :nf])
+        pt, mt = fathom.ingest(k, n)                  # tight rows: ceil(n/64) blocks
+        nb = -(-n // 64)
+        assert np.array_equal(p[..., :nb * 2], pt) and np.array_equal(m[..., :nb], mt)
+        assert not p[..., nb * 2:].any() and not m[..., nb:].any()
+
+
+def test_scan_ragged_n_equals_dequantised_dot():
+    """Full plan, n not a multiple of 64: the scan of the first n tokens equals
+    qbar . (offset + scale * code) with the open block's own scale/offset."""
+    n, d = 64 * 3 + 29, 128
+    k = _keys(n, d, 51)
+    codes, scale, offset = fathom.quantise(k)
+    pl, meta = fathom.ingest(k[None], n, 256)
+    q = np.random.default_rng(52).standard_normal((2, d)).astype(np.float32)
+    depth, qbar = fathom.plan(q, np.ones(d, np.float32), 4 * d)
+    s = fathom.scan(pl[0], meta[0], depth, qbar, n)
+    blk = np.arange(n) // 64
+    ref = (offset.astype(np.float64)[blk] + scale.astype(np.float64)[blk] * codes) @ qbar.astype(np.float64)
+    assert s.shape == (n,) and np.allclose(s, ref, rtol=1e-12, atol=1e-9)
+
+
 # ---------------------------------------------------------------- plan
 def _objective(w, depth):
     return sum(float(w[j]) * 4.0 ** (-int(depth[j])) for j in range(len(w)))
@@ -363,6 +424,27 @@ def test_quest_bound_and_rounding():
         ref = sum(max(float(q[h, j]) * float(mn[b, j]), float(q[h, j]) * float(mx[b, j]))
                   for h in range(4) for j in range(d))
         assert math.isclose(S[b], ref, rel_tol=1e-12, abs_tol=1e-9)
+
+
+def test_quest_open_block_summarised_over_present_tokens():
+    g = np.random.default_rng(19)
+    d, block = 128, 16
+    for n in (1, 7, 16 + 9, 48 + 15):
+        k = _bf16(g.standard_normal((n, d)) * 2)
+        x = fathom.bf16_bits_to_f32(k).astype(np.float64)
+        mn, mx = quest.summaries(k, block)
+        assert mn.shape == (-(-n // block), d)
+        m = n % block or block
+        assert np.all(mn[-1].astype(np.float64) <= x[n - m:].min(0))
+        assert np.all(mx[-1].astype(np.float64) >= x[n - m:].max(0))
+        # outward rounding: the next fp16 inwards would no longer bound the block
+        inner_lo = np.nextafter(mn[-1], np.float16(np.inf)).astype(np.float64)
+        inner_hi = np.nextafter(mx[-1], np.float16(-np.inf)).astype(np.float64)
+        assert np.all(inner_lo > x[n - m:].min(0)) and np.all(inner_hi < x[n - m:].max(0))
+        pad = np.concatenate([k[n - m:], np.repeat(k[n - 1:n], block - m, axis=0)])
+        pm, px = quest.summaries(pad, block)
+        assert np.array_equal(pm[0].view(np.uint16), mn[-1].view(np.uint16))
+        assert np.array_equal(px[0].view(np.uint16), mx[-1].view(np.uint16))
 
 
 def test_quest_exact_when_representable():
