@@ -53,7 +53,9 @@ extern "C" {
 /* Message describing the calling thread's most recent error ("" if none). */
 const char* sdq_last_error(void);
 
-/* ABI version of this header (incremented on incompatible changes). */
+/* ABI version of this header (incremented on incompatible changes).
+ * Version 2: row capacities (n_cap, nb_cap) on every call that reads
+ * per-token cache arrays; fathom_append and minmax_append. */
 int sdq_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -79,6 +81,26 @@ int sdq_abi_version(void);
 int fathom_ingest(const uint16_t* keys, int G, int n, int d, uint32_t* planes, uint32_t* meta,
                   hipStream_t stream);
 
+/* fathom_append -- add a decode step's new keys to a growing bit-plane index
+ * (Fathom summary, bit-plane paragraph; the per-step compressed-key update
+ * of the OasisKV review).  The cache has a fixed row capacity of n_cap
+ * tokens and holds its first n_old + n_new; the call quantises every 64-token
+ * block that holds one of the tokens [n_old, n_old + n_new).  A block whose
+ * tokens are not all present yet (the open block) is quantised over the
+ * tokens it holds, with its own scale and offset, and its absent tokens get
+ * code 0; it is quantised again by later appends until it is full, and is
+ * then identical to what fathom_ingest gives for the same 64 keys.
+ *   keys    bf16 [G][n_cap][d]   key cache, tokens [0, n_old + n_new) valid
+ *   planes  uint32 [G][d][4][n_cap/32]  in/out, the fathom_ingest layout with
+ *           rows n_cap tokens long; blocks before n_old/64 and after the
+ *           last touched block are left as they are.
+ *   meta    uint32 [G][d][n_cap/64]  in/out, likewise.
+ * n_new == 0 is a no-op.
+ * Errors: SDQ_EINVAL on null pointers, G < 1, d != 128, n_cap not a positive
+ * multiple of 64 below 2^25, n_old < 0, n_new < 0, n_old + n_new > n_cap. */
+int fathom_append(const uint16_t* keys, int G, int d, int n_cap, int n_old, int n_new,
+                  uint32_t* planes, uint32_t* meta, hipStream_t stream);
+
 /* minmax_summarize -- per-block min/max key summaries (OasisKV review,
  * Quest-style summaries: one minimum and one maximum vector per logical
  * block, per dimension).
@@ -89,6 +111,18 @@ int fathom_ingest(const uint16_t* keys, int G, int n, int d, uint32_t* planes, u
  * d != 128. */
 int minmax_summarize(const uint16_t* keys, int RG, int n, int d, int block, uint16_t* bmin,
                      uint16_t* bmax, hipStream_t stream);
+
+/* minmax_append -- add new keys to growing min/max summaries (OasisKV
+ * review: summaries are updated as the cache grows).  Rows hold n_cap tokens,
+ * the first n_old + n_new present; every block holding one of the tokens
+ * [n_old, n_old + n_new) is summarised again over its present tokens (a
+ * partly filled last block bounds exactly the keys it holds).
+ *   keys  bf16 [RG][n_cap][d];  bmin, bmax  fp16 [RG][n_cap/block][d] in/out
+ * n_new == 0 is a no-op.
+ * Errors: SDQ_EINVAL on null pointers, RG < 1, d != 128, block < 1, n_cap not
+ * a positive multiple of block, n_old < 0, n_new < 0, n_old + n_new > n_cap. */
+int minmax_append(const uint16_t* keys, int RG, int d, int n_cap, int n_old, int n_new, int block,
+                  uint16_t* bmin, uint16_t* bmax, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Decode step
@@ -132,10 +166,12 @@ int fathom_plan_uniform(const float* q, const float* key_var, int G, int H_grp, 
  *           channel with depth t > 0 the first t planes and the meta row are
  *           written, everything else is left untouched.
  * Run it on a side stream ordered after the plan with events.
- * Errors: SDQ_EINVAL on null pointers, bad sizes (as fathom_ingest), or host
+ * Both layouts have rows of n_cap tokens (fathom_append); the words of the
+ * first n tokens, n rounded up to 64, are copied.
+ * Errors: SDQ_EINVAL on null pointers, bad sizes (as fathom_scan), or host
  * memory the device cannot address. */
 int fathom_gather(const uint32_t* planes_host, const uint32_t* meta_host, const uint8_t* depth,
-                  int G, int d, int n, uint32_t* planes_dev, uint32_t* meta_dev,
+                  int G, int d, int n, int n_cap, uint32_t* planes_dev, uint32_t* meta_dev,
                   hipStream_t stream);
 
 /* fathom_scan -- approximate scores from the plane prefixes.
@@ -148,15 +184,21 @@ int fathom_gather(const uint32_t* planes_host, const uint32_t* meta_host, const 
  * their metadata is not read; depths outside 1..4 count as unread.
  * Accumulation is float32 (each channel's code times its weight is added with
  * one fused multiply-add).
- *   planes, meta  as fathom_ingest;  depth, qbar as fathom_plan
- *   scores        float32 [G][n] out
- *   block_max     float32 [G][n/64] out, or NULL: the maximum score of every
- *                 64-token block (input of topk_select_block_max)
- * Errors: SDQ_EINVAL on null pointers, G < 1, n < 64, n % 64 != 0,
- * n >= 2^25 (one head's planes are addressed with 31-bit offsets), d != 128. */
+ *   planes, meta  as fathom_append: rows of n_cap tokens (n_cap = n for an
+ *                 index built by fathom_ingest); the first n tokens are
+ *                 scored, n any value in [1, n_cap]
+ *   depth, qbar   as fathom_plan
+ *   scores        float32 [G][n64] out, n64 = n rounded up to a multiple of
+ *                 64, 16-byte aligned; tokens [n, n64) (the absent part of
+ *                 an open block) are written as -inf
+ *   block_max     float32 [G][n64/64] out, or NULL: the maximum score of
+ *                 every 64-token block (input of topk_select_block_max)
+ * Errors: SDQ_EINVAL on null pointers, G < 1, n_cap not a positive multiple
+ * of 64, n outside [1, n_cap], n_cap >= 2^25 (one head's planes are addressed
+ * with 31-bit offsets), d != 128, misaligned scores. */
 int fathom_scan(const uint32_t* planes, const uint32_t* meta, const uint8_t* depth,
-                const float* qbar, int G, int d, int n, float* scores, float* block_max,
-                hipStream_t stream);
+                const float* qbar, int G, int d, int n, int n_cap, float* scores,
+                float* block_max, hipStream_t stream);
 
 /* fathom_plan_scan -- fathom_plan (uniform == 0) or fathom_plan_uniform
  * (uniform != 0) followed by fathom_scan, in one launch (Fathom summary,
@@ -167,20 +209,21 @@ int fathom_scan(const uint32_t* planes, const uint32_t* meta, const uint8_t* dep
  * dependent memory round trip from the decode step.
  *   q, key_var, H_grp      as fathom_plan
  *   budget                 budget_bits, or n_channels when uniform != 0
- *   planes, meta, G, d, n  as fathom_scan
+ *   planes, meta, G, d, n, n_cap  as fathom_scan
  *   depth, qbar            out, or both NULL: the plan, as fathom_plan writes it
  *   scores, block_max      as fathom_scan
  * Errors: the union of fathom_plan's and fathom_scan's, and SDQ_EINVAL when
  * exactly one of depth and qbar is NULL. */
 int fathom_plan_scan(const float* q, const float* key_var, int H_grp, int budget, int uniform,
                      const uint32_t* planes, const uint32_t* meta, int G, int d, int n,
-                     uint8_t* depth, float* qbar, float* scores, float* block_max,
+                     int n_cap, uint8_t* depth, float* qbar, float* scores, float* block_max,
                      hipStream_t stream);
 
 /* topk_select -- per-row top-k (HashAttention study notes, sec. 2.1 TOPK and
  * sec. 3.1 fixed positions; OasisKV review, per-KV-head top-K).
- *   keys      [rows][n]: float32 (SDQ_KEY_F32_MAX, largest first; must be
- *             finite, -0 equals +0) or uint8 (SDQ_KEY_U8_MIN, smallest first)
+ *   keys      [rows][n]: float32 (SDQ_KEY_F32_MAX, largest first; not NaN,
+ *             -inf allowed (fathom_scan's pad value), -0 equals +0) or uint8
+ *             (SDQ_KEY_U8_MIN, smallest first)
  *   idx_out   int32 [rows][k + n_sink + n_local] out
  * Per row: positions [0, n_sink) and [n - n_local, n) are always kept and do
  * not compete; the k best of [n_sink, n - n_local) are added, equal keys
@@ -212,19 +255,23 @@ int topk_select_block_max(const float* keys, const float* block_max, int rows, i
 
 /* hamming_scan -- dist[h][i] = popcount(sigs[h][i] XOR qsig[h]) in [0, 32]
  * (HashAttention study notes, sec. 2.2).
- *   sigs uint32 [H][n];  qsig uint32 [H];  dist uint8 [H][n] out
- * Errors: SDQ_EINVAL on null pointers, H < 1, n < 1. */
-int hamming_scan(const uint32_t* sigs, const uint32_t* qsig, int H, int n, uint8_t* dist,
-                 hipStream_t stream);
+ *   sigs uint32 [H][n_cap] (rows of a growing cache, the first n scored);
+ *   qsig uint32 [H];  dist uint8 [H][n] out
+ * Errors: SDQ_EINVAL on null pointers, H < 1, n < 1, n > n_cap. */
+int hamming_scan(const uint32_t* sigs, const uint32_t* qsig, int H, int n, int n_cap,
+                 uint8_t* dist, hipStream_t stream);
 
 /* minmax_block_scan -- block scores against min/max summaries (OasisKV
  * review, Quest-style summaries):
  *   S[rg][b] = sum over the group's heads h and dims j of
  *              max(q[h][j] * bmin[rg][b][j], q[h][j] * bmax[rg][b][j])
- *   bmin, bmax fp16 [RG][nb][d];  q float32 [RG*H_grp][d];  S float32 [RG][nb] out
- * Errors: SDQ_EINVAL on null pointers, RG < 1, H_grp < 1, nb < 1, d != 128. */
+ *   bmin, bmax fp16 [RG][nb_cap][d] (16-byte aligned; the first nb blocks
+ *              of each row are scored);  q float32 [RG*H_grp][d];
+ *   S float32 [RG][nb] out
+ * Errors: SDQ_EINVAL on null pointers, RG < 1, H_grp < 1, nb < 1,
+ * nb > nb_cap, d != 128, misaligned summaries. */
 int minmax_block_scan(const uint16_t* bmin, const uint16_t* bmax, const float* q, int RG, int H_grp,
-                      int nb, int d, float* block_scores, hipStream_t stream);
+                      int nb, int nb_cap, int d, float* block_scores, hipStream_t stream);
 
 /* gather_attend -- renormalised softmax attention over selected rows read by
  * index (HashAttention study notes, sec. 2.1 sparse output formula and
@@ -232,13 +279,13 @@ int minmax_block_scan(const uint16_t* bmin, const uint16_t* bmax, const float* q
  *   o[r][h] = sum_{i in I} e^{z_i} v_i / sum_{i in I} e^{z_i},
  *   z_i = softmax_scale * <q[r][h], K[r][kvh][i]>,  kvh = h / (H_q / H_kv)
  *   q     float32 [R][H_q][d]
- *   K, V  bf16 [R][H_kv][n][d]
+ *   K, V  bf16 [R][H_kv][n_cap][d]: rows of n_cap tokens, the first n valid
  *   idx   int32 [R][H_sel][n_idx], H_sel = H_q if sets_per_query_head else
  *         H_kv (then the H_q/H_kv query heads of a group share the set).
  *         With block_tokens == 1 an entry is a row; with block_tokens > 1 it
  *         is a block id covering rows [b*block_tokens, (b+1)*block_tokens).
  *         Negative entries are padding and are skipped; entries must be
- *         distinct, and entries past the cache end are skipped as well.
+ *         distinct, and entries at or past n are skipped as well.
  *   out   float32 [R][H_q][d]; a set with no valid entry yields zeros.
  *   ws, ws_bytes  workspace of at least gather_attend_workspace_bytes() bytes
  *         (0 when every set fits one workgroup: then ws may be null).  It
@@ -249,13 +296,14 @@ int minmax_block_scan(const uint16_t* bmin, const uint16_t* bmax, const float* q
  * (request, KV head) slice fit 31 bits); H_q / H_kv in {1, 2, 4, 8} when sets
  * are shared; R * H_sel <= 65535.
  * Errors: SDQ_EINVAL on null pointers, R, H_q, H_kv, n, n_idx, block_tokens
- * < 1, H_q % H_kv != 0, d != 128, the limits above, short workspace. */
+ * < 1, n > n_cap, H_q % H_kv != 0, d != 128, the limits above, short
+ * workspace. */
 size_t gather_attend_workspace_bytes(int R, int H_q, int H_kv, int sets_per_query_head, int n_idx,
                                      int block_tokens, int d);
 int gather_attend(const float* q, const uint16_t* K, const uint16_t* V, const int32_t* idx, int R,
-                  int H_q, int H_kv, int sets_per_query_head, int n, int n_idx, int block_tokens,
-                  int d, float softmax_scale, float* out, void* ws, size_t ws_bytes,
-                  hipStream_t stream);
+                  int H_q, int H_kv, int sets_per_query_head, int n, int n_cap, int n_idx,
+                  int block_tokens, int d, float softmax_scale, float* out, void* ws,
+                  size_t ws_bytes, hipStream_t stream);
 
 /* gather_attend_host_kv -- gather_attend with K and V left in host memory
  * (Fathom summary, offloaded setting: the KV rows live in host memory and
@@ -263,14 +311,15 @@ int gather_attend(const float* q, const uint16_t* K, const uint16_t* V, const in
  * kernel reads the selected rows through the buffers' device mapping; no
  * staging copy is made.
  *   K_host, V_host  HOST pointers to pinned, device-mapped memory, bf16
- *                   [R][H_kv][n][d] (16-byte aligned)
+ *                   [R][H_kv][n_cap][d] (16-byte aligned)
  *   everything else as gather_attend (q, idx, out and ws are device memory)
  * Errors: as gather_attend, and SDQ_EINVAL when K_host or V_host is not
  * pinned, device-mapped host memory. */
 int gather_attend_host_kv(const float* q, const uint16_t* K_host, const uint16_t* V_host,
                           const int32_t* idx, int R, int H_q, int H_kv, int sets_per_query_head,
-                          int n, int n_idx, int block_tokens, int d, float softmax_scale,
-                          float* out, void* ws, size_t ws_bytes, hipStream_t stream);
+                          int n, int n_cap, int n_idx, int block_tokens, int d,
+                          float softmax_scale, float* out, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -45,7 +45,7 @@ struct AttendArgs {
   const uint16_t* K;
   const uint16_t* V;
   const int32_t* idx;
-  int R, Hq, Hkv, per_qh, n, n_idx, bt, bt_shift, nblk, rows_per_split;
+  int R, Hq, Hkv, per_qh, n, n_cap, n_idx, bt, bt_shift, nblk, rows_per_split;
   float scale_log2;     // softmax scale * log2(e)
   float* parts;         // partials [R*Hq][nsplit][d + 2] when a set is split (workspace)
   float* out;
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kAtThreads) void attend_kernel(AttendArgs a) {
   const int re = min(M, rb + a.rows_per_split);
   const int nslab = (re - rb + kAtSlab - 1) / kAtSlab;
   const int32_t* sidx = a.idx + size_t(set) * a.n_idx;
-  const size_t slice = (size_t(r) * a.Hkv + kvh) * size_t(a.n) * kHeadDim;
+  const size_t slice = (size_t(r) * a.Hkv + kvh) * size_t(a.n_cap) * kHeadDim;
   const __amdgpu_buffer_rsrc_t Kr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(a.K + slice), (short)0, a.n * 256, 0x00020000);
   const __amdgpu_buffer_rsrc_t Vr = __builtin_amdgcn_make_buffer_rsrc(
@@ -404,23 +404,25 @@ static void launch_attend(dim3 grid, bool pow2, const AttendArgs& a, hipStream_t
 
 static int attend_impl(const char* nm, const float* q, const uint16_t* K, const uint16_t* V,
                        const int32_t* idx, int R, int H_q, int H_kv, int sets_per_query_head,
-                       int n, int n_idx, int block_tokens, int d, float softmax_scale,
+                       int n, int n_cap, int n_idx, int block_tokens, int d, float softmax_scale,
                        float* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 extern "C" int gather_attend(const float* q, const uint16_t* K, const uint16_t* V,
                              const int32_t* idx, int R, int H_q, int H_kv, int sets_per_query_head,
-                             int n, int n_idx, int block_tokens, int d, float softmax_scale,
-                             float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
-  return attend_impl("gather_attend", q, K, V, idx, R, H_q, H_kv, sets_per_query_head, n, n_idx,
-                     block_tokens, d, softmax_scale, out, ws, ws_bytes, stream);
+                             int n, int n_cap, int n_idx, int block_tokens, int d,
+                             float softmax_scale, float* out, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  return attend_impl("gather_attend", q, K, V, idx, R, H_q, H_kv, sets_per_query_head, n, n_cap,
+                     n_idx, block_tokens, d, softmax_scale, out, ws, ws_bytes, stream);
 }
 
 // K and V stay in pinned host memory: the same kernel reads the selected rows
 // through the buffers' device mapping, over the host link.
 extern "C" int gather_attend_host_kv(const float* q, const uint16_t* K_host,
                                      const uint16_t* V_host, const int32_t* idx, int R, int H_q,
-                                     int H_kv, int sets_per_query_head, int n, int n_idx,
-                                     int block_tokens, int d, float softmax_scale, float* out,
+                                     int H_kv, int sets_per_query_head, int n, int n_cap,
+                                     int n_idx, int block_tokens, int d, float softmax_scale,
+                                     float* out,
                                      void* ws, size_t ws_bytes, hipStream_t stream) {
   SDQ_REQUIRE(K_host && V_host, "gather_attend_host_kv: null pointer");
   void* kd = nullptr;
@@ -433,14 +435,15 @@ extern "C" int gather_attend_host_kv(const float* q, const uint16_t* K_host,
   }
   return attend_impl("gather_attend_host_kv", q, static_cast<const uint16_t*>(kd),
                      static_cast<const uint16_t*>(vd), idx, R, H_q, H_kv, sets_per_query_head, n,
-                     n_idx, block_tokens, d, softmax_scale, out, ws, ws_bytes, stream);
+                     n_cap, n_idx, block_tokens, d, softmax_scale, out, ws, ws_bytes, stream);
 }
 
 static int attend_impl(const char* nm, const float* q, const uint16_t* K, const uint16_t* V,
                        const int32_t* idx, int R, int H_q, int H_kv, int sets_per_query_head,
-                       int n, int n_idx, int block_tokens, int d, float softmax_scale,
+                       int n, int n_cap, int n_idx, int block_tokens, int d, float softmax_scale,
                        float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
   SDQ_REQUIRE(q && K && V && idx && out, "%s: null pointer", nm);
+  SDQ_REQUIRE(n <= n_cap, "%s: n=%d exceeds the row capacity n_cap=%d", nm, n, n_cap);
   SDQ_REQUIRE(R >= 1 && H_q >= 1 && H_kv >= 1 && n >= 1 && n_idx >= 1 && block_tokens >= 1,
               "%s: R, H_q, H_kv, n, n_idx, block_tokens must be >= 1", nm);
   SDQ_REQUIRE(reinterpret_cast<uintptr_t>(K) % 16 == 0 && reinterpret_cast<uintptr_t>(V) % 16 == 0,
@@ -467,7 +470,7 @@ static int attend_impl(const char* nm, const float* q, const uint16_t* K, const 
   int shift = 0;
   while ((1 << shift) < block_tokens && shift < 30) ++shift;
   const int nblk = int((n + (long long)block_tokens - 1) / block_tokens);
-  AttendArgs a{q, K, V, idx, R, H_q, H_kv, sets_per_query_head ? 1 : 0, n, n_idx, block_tokens,
+  AttendArgs a{q, K, V, idx, R, H_q, H_kv, sets_per_query_head ? 1 : 0, n, n_cap, n_idx, block_tokens,
                shift, nblk, int(per), softmax_scale * 1.4426950408889634f,
                reinterpret_cast<float*>(ws), out};
   const dim3 grid{unsigned(nsplit), unsigned(sets), 1u};

@@ -3,30 +3,43 @@
 //    planes (Fathom summary, bit-plane paragraph);
 //  * minmax_summarize: per-block min/max key summaries (OasisKV review,
 //    Quest-style block summaries).
-// Both run once per cached block, before any decode step; they are not part
-// of the timed decode path.
+// Both build a whole index before decoding; fathom_append and minmax_append
+// add a decode step's new tokens to a cache of fixed row capacity, quantising
+// (or summarising) the open block again until it is full.  None of them is
+// part of the timed decode path.
 #include "common.hpp"
 
 namespace sdq {
 
 // One thread owns a pair of adjacent channels; the 64 threads of a wave cover
 // the 128 channels, so each token row (256 bytes) is read by one coalesced
-// 4-byte-per-lane load.  A workgroup walks `bpw` consecutive 64-token blocks.
-
-__global__ __launch_bounds__(64) void fathom_ingest_kernel(const uint32_t* __restrict__ keys,
-                                                           int n, int nb64, int bpw,
-                                                           uint32_t* __restrict__ planes,
+// 4-byte-per-lane load.  A workgroup walks `bpw` consecutive 64-token blocks
+// of the range [b0, b0 + nblk).
+//
+// Rows are n_cap tokens long (the cache's capacity) and the first n tokens
+// are present.  A partly filled last block (the open block of a growing
+// cache) is quantised over its m present tokens: loads past them repeat the
+// last present row, which leaves the block's min and max unchanged, and the
+// absent tokens' plane bits are cleared.
+__global__ __launch_bounds__(64) void fathom_append_kernel(const uint32_t* __restrict__ keys,
+                                                           int n_cap, int n, int b0, int nblk,
+                                                           int bpw, uint32_t* __restrict__ planes,
                                                            uint32_t* __restrict__ meta) {
   const int g = blockIdx.y;
   const int pair = threadIdx.x;
-  const size_t nw = size_t(n) / 32;                       // 32-token words per plane row
+  const size_t nw = size_t(n_cap) / 32;                   // 32-token words per plane row
+  const int nb_cap = n_cap / 64;
   for (int bb = 0; bb < bpw; ++bb) {
-    const int b = blockIdx.x * bpw + bb;
-    if (b >= nb64) break;
-    const uint32_t* src = keys + (size_t(g) * n + size_t(b) * 64) * (kHeadDim / 2) + pair;
+    const int bi = blockIdx.x * bpw + bb;
+    if (bi >= nblk) break;
+    const int b = b0 + bi;
+    const int m = n - b * 64 < 64 ? n - b * 64 : 64;       // present tokens, >= 1
+    const uint32_t* src = keys + (size_t(g) * n_cap + size_t(b) * 64) * (kHeadDim / 2) + pair;
     uint32_t w[64];
 #pragma unroll
-    for (int i = 0; i < 64; ++i) w[i] = src[size_t(i) * (kHeadDim / 2)];
+    for (int i = 0; i < 64; ++i) w[i] = src[size_t(i < m ? i : m - 1) * (kHeadDim / 2)];
+    const uint32_t keep0 = m >= 32 ? 0xFFFFFFFFu : (1u << m) - 1u;
+    const uint32_t keep1 = m >= 64 ? 0xFFFFFFFFu : (m > 32 ? (1u << (m - 32)) - 1u : 0u);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       float mn = INFINITY, mx = -INFINITY;
@@ -54,10 +67,10 @@ __global__ __launch_bounds__(64) void fathom_ingest_kernel(const uint32_t* __res
       uint32_t* prow = planes + (size_t(g) * kHeadDim + j) * 4 * nw;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        prow[size_t(p) * nw + 2 * size_t(b)] = pl[p][0];
-        prow[size_t(p) * nw + 2 * size_t(b) + 1] = pl[p][1];
+        prow[size_t(p) * nw + 2 * size_t(b)] = pl[p][0] & keep0;
+        prow[size_t(p) * nw + 2 * size_t(b) + 1] = pl[p][1] & keep1;
       }
-      meta[(size_t(g) * kHeadDim + j) * nb64 + b] =
+      meta[(size_t(g) * kHeadDim + j) * nb_cap + b] =
           uint32_t(__builtin_bit_cast(uint16_t, sc16)) |
           (uint32_t(__builtin_bit_cast(uint16_t, off16)) << 16);
     }
@@ -83,19 +96,25 @@ __device__ __forceinline__ uint32_t f16_round_up(float x) {
   return half_bits_to_f32(h) < x ? f16_next_up(h) : h;
 }
 
-// One thread per adjacent channel pair; a workgroup walks `bpw` blocks.
-__global__ __launch_bounds__(64) void minmax_summarize_kernel(const uint32_t* __restrict__ keys,
-                                                              int n, int block, int nb, int bpw,
-                                                              uint32_t* __restrict__ bmin,
-                                                              uint32_t* __restrict__ bmax) {
+// One thread per adjacent channel pair; a workgroup walks `bpw` blocks of the
+// range [b0, b0 + nblk).  Rows are n_cap tokens long with the first n
+// present; a partly filled last block is summarised over its present tokens.
+__global__ __launch_bounds__(64) void minmax_append_kernel(const uint32_t* __restrict__ keys,
+                                                           int n_cap, int n, int block, int b0,
+                                                           int nblk, int bpw,
+                                                           uint32_t* __restrict__ bmin,
+                                                           uint32_t* __restrict__ bmax) {
   const int rg = blockIdx.y;
   const int pair = threadIdx.x;
+  const int nb_cap = n_cap / block;
   for (int bb = 0; bb < bpw; ++bb) {
-    const int b = blockIdx.x * bpw + bb;
-    if (b >= nb) break;
-    const uint32_t* src = keys + (size_t(rg) * n + size_t(b) * block) * (kHeadDim / 2) + pair;
+    const int bi = blockIdx.x * bpw + bb;
+    if (bi >= nblk) break;
+    const int b = b0 + bi;
+    const int m = n - b * block < block ? n - b * block : block;
+    const uint32_t* src = keys + (size_t(rg) * n_cap + size_t(b) * block) * (kHeadDim / 2) + pair;
     float lo0 = INFINITY, lo1 = INFINITY, hi0 = -INFINITY, hi1 = -INFINITY;
-    for (int i = 0; i < block; ++i) {
+    for (int i = 0; i < m; ++i) {
       const uint32_t w = src[size_t(i) * (kHeadDim / 2)];
       const float a = bf16_lo(w), c = bf16_hi(w);
       lo0 = fminf(lo0, a);
@@ -103,7 +122,7 @@ __global__ __launch_bounds__(64) void minmax_summarize_kernel(const uint32_t* __
       lo1 = fminf(lo1, c);
       hi1 = fmaxf(hi1, c);
     }
-    const size_t o = (size_t(rg) * nb + b) * (kHeadDim / 2) + pair;
+    const size_t o = (size_t(rg) * nb_cap + b) * (kHeadDim / 2) + pair;
     bmin[o] = f16_round_down(lo0) | (f16_round_down(lo1) << 16);
     bmax[o] = f16_round_up(hi0) | (f16_round_up(hi1) << 16);
   }
@@ -113,18 +132,48 @@ __global__ __launch_bounds__(64) void minmax_summarize_kernel(const uint32_t* __
 
 using namespace sdq;
 
+static void launch_fathom_append(const uint16_t* keys, int G, int n_cap, int n, int b0, int nblk,
+                                 uint32_t* planes, uint32_t* meta, hipStream_t stream) {
+  const int bpw = 4;
+  dim3 grid(cdiv(nblk, bpw), G);
+  hipLaunchKernelGGL(fathom_append_kernel, grid, dim3(64), 0, stream,
+                     reinterpret_cast<const uint32_t*>(keys), n_cap, n, b0, nblk, bpw, planes, meta);
+}
+
 extern "C" int fathom_ingest(const uint16_t* keys, int G, int n, int d, uint32_t* planes,
                              uint32_t* meta, hipStream_t stream) {
   SDQ_REQUIRE(keys && planes && meta, "fathom_ingest: null pointer");
   SDQ_REQUIRE(G >= 1, "fathom_ingest: G=%d must be >= 1", G);
   SDQ_REQUIRE(n >= 64 && n % 64 == 0, "fathom_ingest: n=%d must be a positive multiple of 64", n);
+  SDQ_REQUIRE(n < (1 << 25), "fathom_ingest: n=%d must be below 2^25", n);
   SDQ_REQUIRE(d == kHeadDim, "fathom_ingest: d=%d unsupported (only 128)", d);
-  const int nb64 = n / 64;
-  const int bpw = 4;
-  dim3 grid(cdiv(nb64, bpw), G);
-  hipLaunchKernelGGL(fathom_ingest_kernel, grid, dim3(64), 0, stream,
-                     reinterpret_cast<const uint32_t*>(keys), n, nb64, bpw, planes, meta);
+  launch_fathom_append(keys, G, n, n, 0, n / 64, planes, meta, stream);
   return check_launch("fathom_ingest");
+}
+
+extern "C" int fathom_append(const uint16_t* keys, int G, int d, int n_cap, int n_old, int n_new,
+                             uint32_t* planes, uint32_t* meta, hipStream_t stream) {
+  SDQ_REQUIRE(keys && planes && meta, "fathom_append: null pointer");
+  SDQ_REQUIRE(G >= 1, "fathom_append: G=%d must be >= 1", G);
+  SDQ_REQUIRE(d == kHeadDim, "fathom_append: d=%d unsupported (only 128)", d);
+  SDQ_REQUIRE(n_cap >= 64 && n_cap % 64 == 0 && n_cap < (1 << 25),
+              "fathom_append: n_cap=%d must be a positive multiple of 64 below 2^25", n_cap);
+  SDQ_REQUIRE(n_old >= 0 && n_new >= 0 && (long long)n_old + n_new <= n_cap,
+              "fathom_append: n_old=%d + n_new=%d must fit n_cap=%d", n_old, n_new, n_cap);
+  if (n_new == 0) return SDQ_OK;
+  const int n = n_old + n_new;
+  const int b0 = n_old / 64;
+  launch_fathom_append(keys, G, n_cap, n, b0, (n + 63) / 64 - b0, planes, meta, stream);
+  return check_launch("fathom_append");
+}
+
+static void launch_minmax_append(const uint16_t* keys, int RG, int n_cap, int n, int block, int b0,
+                                 int nblk, uint16_t* bmin, uint16_t* bmax, hipStream_t stream) {
+  const int bpw = 8;
+  dim3 grid(cdiv(nblk, bpw), RG);
+  hipLaunchKernelGGL(minmax_append_kernel, grid, dim3(64), 0, stream,
+                     reinterpret_cast<const uint32_t*>(keys), n_cap, n, block, b0, nblk, bpw,
+                     reinterpret_cast<uint32_t*>(bmin), reinterpret_cast<uint32_t*>(bmax));
 }
 
 extern "C" int minmax_summarize(const uint16_t* keys, int RG, int n, int d, int block,
@@ -134,11 +183,23 @@ extern "C" int minmax_summarize(const uint16_t* keys, int RG, int n, int d, int 
   SDQ_REQUIRE(block >= 1 && n >= block && n % block == 0,
               "minmax_summarize: n=%d must be a positive multiple of block=%d", n, block);
   SDQ_REQUIRE(d == kHeadDim, "minmax_summarize: d=%d unsupported (only 128)", d);
-  const int nb = n / block;
-  const int bpw = 8;
-  dim3 grid(cdiv(nb, bpw), RG);
-  hipLaunchKernelGGL(minmax_summarize_kernel, grid, dim3(64), 0, stream,
-                     reinterpret_cast<const uint32_t*>(keys), n, block, nb, bpw,
-                     reinterpret_cast<uint32_t*>(bmin), reinterpret_cast<uint32_t*>(bmax));
+  launch_minmax_append(keys, RG, n, n, block, 0, n / block, bmin, bmax, stream);
   return check_launch("minmax_summarize");
+}
+
+extern "C" int minmax_append(const uint16_t* keys, int RG, int d, int n_cap, int n_old, int n_new,
+                             int block, uint16_t* bmin, uint16_t* bmax, hipStream_t stream) {
+  SDQ_REQUIRE(keys && bmin && bmax, "minmax_append: null pointer");
+  SDQ_REQUIRE(RG >= 1, "minmax_append: RG=%d must be >= 1", RG);
+  SDQ_REQUIRE(d == kHeadDim, "minmax_append: d=%d unsupported (only 128)", d);
+  SDQ_REQUIRE(block >= 1 && n_cap >= block && n_cap % block == 0,
+              "minmax_append: n_cap=%d must be a positive multiple of block=%d", n_cap, block);
+  SDQ_REQUIRE(n_old >= 0 && n_new >= 0 && (long long)n_old + n_new <= n_cap,
+              "minmax_append: n_old=%d + n_new=%d must fit n_cap=%d", n_old, n_new, n_cap);
+  if (n_new == 0) return SDQ_OK;
+  const int n = n_old + n_new;
+  const int b0 = n_old / block;
+  launch_minmax_append(keys, RG, n_cap, n, block, b0, (n + block - 1) / block - b0, bmin, bmax,
+                       stream);
+  return check_launch("minmax_append");
 }

@@ -26,7 +26,7 @@ __device__ __forceinline__ float fma_h(uint32_t w, int hi, float a, float acc) {
 
 __global__ __launch_bounds__(kMmThreads) void minmax_block_scan_kernel(
     const uint4* __restrict__ bmin, const uint4* __restrict__ bmax, const float* __restrict__ q,
-    int Hgrp, int nb, float* __restrict__ S) {
+    int Hgrp, int nb, int nb_cap, float* __restrict__ S) {
   const int rg = blockIdx.y;
   const int tid = threadIdx.x;
   const int sub = tid & 15;             // which 8 dimensions
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kMmThreads) void minmax_block_scan_kernel(
       N[e] += fminf(v, 0.0f);
     }
   }
-  const size_t row = size_t(rg) * nb;
+  const size_t row = size_t(rg) * nb_cap;          // summaries; scores rows are nb long
   // every step's summaries are requested before the first is used (the
   // index is clamped so the loads stay unconditional and in bounds)
   uint4 lo[kMmIters], hi[kMmIters];
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kMmThreads) void minmax_block_scan_kernel(
       acc = fma_h(lw[e], 1, N[2 * e + 1], acc);
     }
     acc = row16_sum(acc);                      // the block's 16 lanes form one DPP row
-    if (sub == 0 && b < nb) S[row + b] = acc;
+    if (sub == 0 && b < nb) S[size_t(rg) * nb + b] = acc;
   }
 }
 
@@ -80,17 +80,18 @@ __global__ __launch_bounds__(kMmThreads) void minmax_block_scan_kernel(
 using namespace sdq;
 
 extern "C" int minmax_block_scan(const uint16_t* bmin, const uint16_t* bmax, const float* q,
-                                 int RG, int H_grp, int nb, int d, float* block_scores,
-                                 hipStream_t stream) {
+                                 int RG, int H_grp, int nb, int nb_cap, int d,
+                                 float* block_scores, hipStream_t stream) {
   SDQ_REQUIRE(bmin && bmax && q && block_scores, "minmax_block_scan: null pointer");
   SDQ_REQUIRE(RG >= 1 && H_grp >= 1 && nb >= 1, "minmax_block_scan: RG=%d, H_grp=%d, nb=%d must be >= 1",
               RG, H_grp, nb);
+  SDQ_REQUIRE(nb <= nb_cap, "minmax_block_scan: nb=%d exceeds nb_cap=%d", nb, nb_cap);
   SDQ_REQUIRE(d == kHeadDim, "minmax_block_scan: d=%d unsupported (only 128)", d);
   SDQ_REQUIRE(reinterpret_cast<uintptr_t>(bmin) % 16 == 0 && reinterpret_cast<uintptr_t>(bmax) % 16 == 0,
               "minmax_block_scan: summaries must be 16-byte aligned");
   dim3 grid(cdiv(nb, kMmIters * kMmBlocksPerIter), RG);
   hipLaunchKernelGGL(minmax_block_scan_kernel, grid, dim3(kMmThreads), 0, stream,
                      reinterpret_cast<const uint4*>(bmin), reinterpret_cast<const uint4*>(bmax), q,
-                     H_grp, nb, block_scores);
+                     H_grp, nb, nb_cap, block_scores);
   return check_launch("minmax_block_scan");
 }

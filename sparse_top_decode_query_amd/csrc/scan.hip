@@ -29,6 +29,11 @@
 // Optionally the maximum score of every 64-token block is written as well
 // (the two lanes of a block combine theirs); top-k selection uses it to skip
 // blocks that cannot hold a winner.
+//
+// A growing cache: plane rows hold n_cap tokens, the first n are scored, and
+// n need not be a multiple of 64.  Score rows are n rounded up to 64 long;
+// the tokens past n in the open block score -inf, so they never reach a block
+// maximum or the top-k.
 #include "common.hpp"
 #include "plan_dev.hpp"
 
@@ -50,7 +55,7 @@ struct ChanData {
 struct ScanSrc {
   __amdgpu_buffer_rsrc_t planes, meta;
   uint32_t plane_off, meta_off;   // this lane's word / block, in bytes
-  uint32_t row_bytes, mrow_bytes;   // one plane row (n/8 bytes), one metadata row (n/16)
+  uint32_t row_bytes, mrow_bytes;   // one plane row (n_cap/8 bytes), one metadata row (n_cap/16)
 };
 
 template <int T>
@@ -159,7 +164,7 @@ struct PlanIn {
 template <int MODE>
 __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
     const uint32_t* __restrict__ planes, const uint32_t* __restrict__ meta,
-    const uint8_t* __restrict__ depth, const float* __restrict__ qbar, int n, int nb64,
+    const uint8_t* __restrict__ depth, const float* __restrict__ qbar, int n, int nb64, int n_cap,
     float* __restrict__ scores, float* __restrict__ block_max, PlanIn pin) {
   __shared__ float s_q2[kHeadDim];
   __shared__ int s_j[kHeadDim];
@@ -231,20 +236,22 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
   }
   __syncthreads();
 
-  const size_t nw = size_t(n) / 32;
+  const size_t nw = size_t(nb64) * 2;                            // words scored (n rounded up to 64)
+  const size_t nw_cap = size_t(n_cap) / 32;                       // words per plane row
   const int wd = (blockIdx.x * kScanWaves + wave) * 64 + lane;   // this lane's 32-token word
   if ((blockIdx.x * kScanWaves + wave) * 64 >= int(nw)) return;   // whole wave past the end
   const bool valid = wd < int(nw);
   const int wdc = valid ? wd : int(nw) - 1;                       // loads stay in bounds
   const int b = wdc >> 1;
   ScanSrc src;
-  src.row_bytes = uint32_t(nw) * 4u;
-  src.mrow_bytes = uint32_t(nb64) * 4u;
+  src.row_bytes = uint32_t(nw_cap) * 4u;
+  src.mrow_bytes = uint32_t(n_cap / 64) * 4u;
   src.planes = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint32_t*>(planes + size_t(g) * kHeadDim * 4 * nw), (short)0,
+      const_cast<uint32_t*>(planes + size_t(g) * kHeadDim * 4 * nw_cap), (short)0,
       int(kHeadDim * 4 * src.row_bytes), 0x00020000);
-  src.meta = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(meta + size_t(g) * kHeadDim * nb64),
-                                               (short)0, int(kHeadDim * src.mrow_bytes), 0x00020000);
+  src.meta = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(meta + size_t(g) * kHeadDim * (n_cap / 64)), (short)0,
+      int(kHeadDim * src.mrow_bytes), 0x00020000);
   src.plane_off = uint32_t(wdc) * 4u;
   src.meta_off = uint32_t(b) * 4u;
 
@@ -267,8 +274,14 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
   for (int i = 0; i < kTok; ++i) {
     const int pos = (i & 15) < 8 ? (i & 15) : (i & 15) - 8;    // acc[i] holds 2^pos x its sum
     sv[i] = __builtin_fmaf(acc[i], __builtin_bit_cast(float, uint32_t(127 - pos) << 23), C);
-    m = fmaxf(m, sv[i]);
   }
+  const int wbase = (blockIdx.x * kScanWaves + wave) * 64;       // first word of the wave
+  if ((wbase + 64) * kTok > n) {                                  // the wave holds tokens past n
+#pragma unroll
+    for (int i = 0; i < kTok; ++i) sv[i] = wd * kTok + i < n ? sv[i] : -INFINITY;
+  }
+#pragma unroll
+  for (int i = 0; i < kTok; ++i) m = fmaxf(m, sv[i]);
   // Scores leave through LDS so that every store instruction writes 1 KB of
   // consecutive tokens (lane l holds tokens 32l..32l+31 of the wave's range).
   float4* so = s_out[wave];
@@ -278,9 +291,8 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const int wbase = (blockIdx.x * kScanWaves + wave) * 64;       // first word of the wave
   const int nvalid = int(nw) - wbase < 64 ? int(nw) - wbase : 64; // words of the wave in range
-  float4* dst = reinterpret_cast<float4*>(scores + size_t(g) * n + size_t(wbase) * kTok);
+  float4* dst = reinterpret_cast<float4*>(scores + size_t(g) * nb64 * 64 + size_t(wbase) * kTok);
 #pragma unroll
   for (int v = 0; v < kTok / 4; ++v) {
     const int f = v * 64 + lane;                                  // float4 index in the wave's range
@@ -298,32 +310,34 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
 using namespace sdq;
 
 static int scan_checks(const char* nm, const uint32_t* planes, const uint32_t* meta, int G,
-                       int d, int n, const float* scores) {
+                       int d, int n, int n_cap, const float* scores) {
   SDQ_REQUIRE(planes && meta && scores, "%s: null pointer", nm);
   SDQ_REQUIRE(G >= 1, "%s: G=%d must be >= 1", nm, G);
-  SDQ_REQUIRE(n >= 64 && n % 64 == 0, "%s: n=%d must be a positive multiple of 64", nm, n);
-  SDQ_REQUIRE(n < (1 << 25), "%s: n=%d must be below 2^25 (a head's planes fit 2 GiB)", nm, n);
+  SDQ_REQUIRE(n_cap >= 64 && n_cap % 64 == 0, "%s: n_cap=%d must be a positive multiple of 64", nm,
+              n_cap);
+  SDQ_REQUIRE(n >= 1 && n <= n_cap, "%s: n=%d must be in [1, n_cap=%d]", nm, n, n_cap);
+  SDQ_REQUIRE(n_cap < (1 << 25), "%s: n_cap=%d must be below 2^25 (a head's planes fit 2 GiB)", nm,
+              n_cap);
   SDQ_REQUIRE(d == kHeadDim, "%s: d=%d unsupported (only 128)", nm, d);
   SDQ_REQUIRE(reinterpret_cast<uintptr_t>(scores) % 16 == 0, "%s: scores must be 16-byte aligned", nm);
   return SDQ_OK;
 }
 
 extern "C" int fathom_scan(const uint32_t* planes, const uint32_t* meta, const uint8_t* depth,
-                           const float* qbar, int G, int d, int n, float* scores, float* block_max,
-                           hipStream_t stream) {
+                           const float* qbar, int G, int d, int n, int n_cap, float* scores,
+                           float* block_max, hipStream_t stream) {
   SDQ_REQUIRE(depth && qbar, "fathom_scan: null pointer");
-  if (const int rc = scan_checks("fathom_scan", planes, meta, G, d, n, scores)) return rc;
-  const int nb64 = n / 64;
-  const size_t nw = size_t(n) / 32;
-  dim3 grid(cdiv(nw, kScanWaves * 64), G);
+  if (const int rc = scan_checks("fathom_scan", planes, meta, G, d, n, n_cap, scores)) return rc;
+  const int nb64 = (n + 63) / 64;
+  dim3 grid(cdiv(size_t(nb64) * 2, kScanWaves * 64), G);
   hipLaunchKernelGGL(fathom_scan_kernel<0>, grid, dim3(kScanWaves * 64), 0, stream, planes, meta,
-                     depth, qbar, n, nb64, scores, block_max, PlanIn{});
+                     depth, qbar, n, nb64, n_cap, scores, block_max, PlanIn{});
   return check_launch("fathom_scan");
 }
 
 extern "C" int fathom_plan_scan(const float* q, const float* key_var, int H_grp, int budget,
                                 int uniform, const uint32_t* planes, const uint32_t* meta, int G,
-                                int d, int n, uint8_t* depth, float* qbar, float* scores,
+                                int d, int n, int n_cap, uint8_t* depth, float* qbar, float* scores,
                                 float* block_max, hipStream_t stream) {
   SDQ_REQUIRE(q && key_var, "fathom_plan_scan: null pointer");
   SDQ_REQUIRE((depth == nullptr) == (qbar == nullptr),
@@ -331,16 +345,15 @@ extern "C" int fathom_plan_scan(const float* q, const float* key_var, int H_grp,
   SDQ_REQUIRE(H_grp >= 1, "fathom_plan_scan: H_grp=%d must be >= 1", H_grp);
   SDQ_REQUIRE(budget >= 0, "fathom_plan_scan: budget/channel count %d must be >= 0", budget);
   SDQ_REQUIRE(!uniform || budget <= d, "fathom_plan_scan: n_channels=%d exceeds d=%d", budget, d);
-  if (const int rc = scan_checks("fathom_plan_scan", planes, meta, G, d, n, scores)) return rc;
-  const int nb64 = n / 64;
-  const size_t nw = size_t(n) / 32;
-  dim3 grid(cdiv(nw, kScanWaves * 64), G);
+  if (const int rc = scan_checks("fathom_plan_scan", planes, meta, G, d, n, n_cap, scores)) return rc;
+  const int nb64 = (n + 63) / 64;
+  dim3 grid(cdiv(size_t(nb64) * 2, kScanWaves * 64), G);
   const PlanIn pin{q, key_var, H_grp, budget, depth, qbar};
   if (uniform)
     hipLaunchKernelGGL(fathom_scan_kernel<2>, grid, dim3(kScanWaves * 64), 0, stream, planes, meta,
-                       nullptr, nullptr, n, nb64, scores, block_max, pin);
+                       nullptr, nullptr, n, nb64, n_cap, scores, block_max, pin);
   else
     hipLaunchKernelGGL(fathom_scan_kernel<1>, grid, dim3(kScanWaves * 64), 0, stream, planes, meta,
-                       nullptr, nullptr, n, nb64, scores, block_max, pin);
+                       nullptr, nullptr, n, nb64, n_cap, scores, block_max, pin);
   return check_launch("fathom_plan_scan");
 }

@@ -28,23 +28,25 @@ _SIGS = {
     "sdq_last_error": ([], ctypes.c_char_p),
     "sdq_abi_version": ([], _c_int),
     "fathom_ingest": ([_vp, _c_int, _c_int, _c_int, _vp, _vp, _vp], _c_int),
+    "fathom_append": ([_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp], _c_int),
     "minmax_summarize": ([_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp], _c_int),
+    "minmax_append": ([_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp], _c_int),
     "fathom_plan": ([_vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp], _c_int),
     "fathom_plan_uniform": ([_vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp], _c_int),
-    "fathom_gather": ([_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp], _c_int),
-    "fathom_scan": ([_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp], _c_int),
-    "fathom_plan_scan": ([_vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp,
-                          _vp, _vp], _c_int),
+    "fathom_gather": ([_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp], _c_int),
+    "fathom_scan": ([_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp], _c_int),
+    "fathom_plan_scan": ([_vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp,
+                          _vp, _vp, _vp, _vp], _c_int),
     "topk_select_block_max": ([_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp], _c_int),
     "topk_select_workspace_bytes": ([_c_int, _c_int, _c_int, _c_int], _c_size),
     "topk_select": ([_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _c_size, _vp], _c_int),
-    "hamming_scan": ([_vp, _vp, _c_int, _c_int, _vp, _vp], _c_int),
-    "minmax_block_scan": ([_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp], _c_int),
+    "hamming_scan": ([_vp, _vp, _c_int, _c_int, _c_int, _vp, _vp], _c_int),
+    "minmax_block_scan": ([_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp], _c_int),
     "gather_attend_workspace_bytes": ([_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int], _c_size),
-    "gather_attend": ([_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+    "gather_attend": ([_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                        _c_int, _f, _vp, _vp, _c_size, _vp], _c_int),
     "gather_attend_host_kv": ([_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
-                       _c_int, _f, _vp, _vp, _c_size, _vp], _c_int),
+                               _c_int, _c_int, _f, _vp, _vp, _c_size, _vp], _c_int),
 }
 
 
@@ -106,14 +108,53 @@ def _out(t, shape, dtype, device, name, elem):
 
 # ------------------------------------------------------------------ ingest
 class PlaneIndex:
-    """The bit-plane index of one layer: planes uint32 [G][128][4][n/32] and
-    meta uint32 [G][128][n/64]."""
+    """The bit-plane index of one layer: planes uint32 [G][128][4][n_cap/32]
+    and meta uint32 [G][128][n_cap/64], rows of n_cap tokens (n_cap = n for
+    an index built in one go)."""
 
     def __init__(self, planes, meta):
         self.planes, self.meta = planes, meta
 
+    @property
+    def n_cap(self) -> int:
+        return self.planes.shape[-1] * 32
+
     def __iter__(self):
         return iter((self.planes, self.meta))
+
+
+def _round64(n: int) -> int:
+    return -(-int(n) // 64) * 64
+
+
+def plane_index_empty(G, n_cap, device="cuda"):
+    """An index of row capacity n_cap (a multiple of 64) for fathom_append."""
+    if n_cap % 64:
+        raise SDQError("n_cap must be a multiple of 64")
+    return PlaneIndex(torch.zeros(G, D, 4, n_cap // 32, dtype=torch.int32, device=device),
+                      torch.zeros(G, D, n_cap // 64, dtype=torch.int32, device=device))
+
+
+def _index_sizes(planes, meta, G, d):
+    if planes.dim() != 4 or planes.shape[:3] != (G, d, 4):
+        raise SDQError("planes must be [G][128][4][n_cap/32]")
+    n_cap = planes.shape[3] * 32
+    _dev(planes, "planes", 4, G * d * 4 * (n_cap // 32))
+    _dev(meta, "meta", 4, G * d * (n_cap // 64))
+    return n_cap
+
+
+def fathom_append(keys, n_old, n_new, index, stream=None):
+    """keys bf16 [G][n_cap][128] (the key cache, first n_old + n_new tokens
+    valid) -> index updated in place over the blocks the new tokens touch."""
+    G, n_cap, d = keys.shape
+    _dev(keys, "keys", 2)
+    if _index_sizes(index.planes, index.meta, G, d) != n_cap:
+        raise SDQError("keys and index have different row capacities")
+    _check(load().fathom_append(_vp(keys.data_ptr()), G, d, n_cap, int(n_old), int(n_new),
+                                _vp(index.planes.data_ptr()), _vp(index.meta.data_ptr()),
+                                _stream(stream)), "fathom_append")
+    return index
 
 
 def fathom_ingest(keys, planes=None, meta=None, stream=None):
@@ -125,6 +166,19 @@ def fathom_ingest(keys, planes=None, meta=None, stream=None):
     _check(load().fathom_ingest(_vp(keys.data_ptr()), G, n, d, _vp(planes.data_ptr()),
                                 _vp(meta.data_ptr()), _stream(stream)), "fathom_ingest")
     return PlaneIndex(planes, meta)
+
+
+def minmax_append(keys, n_old, n_new, bmin, bmax, block=16, stream=None):
+    """keys bf16 [RG][n_cap][128] -> bmin, bmax fp16 bits [RG][n_cap/block][128]
+    updated in place over the blocks the new tokens touch."""
+    RG, n_cap, d = keys.shape
+    _dev(keys, "keys", 2)
+    _dev(bmin, "bmin", 2, RG * (n_cap // block) * d)
+    _dev(bmax, "bmax", 2, RG * (n_cap // block) * d)
+    _check(load().minmax_append(_vp(keys.data_ptr()), RG, d, n_cap, int(n_old), int(n_new), block,
+                                _vp(bmin.data_ptr()), _vp(bmax.data_ptr()), _stream(stream)),
+           "minmax_append")
+    return bmin, bmax
 
 
 def minmax_summarize(keys, block=16, bmin=None, bmax=None, stream=None):
@@ -162,41 +216,44 @@ def fathom_plan(q, key_var, budget_bits, depth=None, qbar=None, uniform_channels
     return depth, qbar
 
 
-def fathom_gather(planes_host, meta_host, depth, planes_dev, meta_dev, stream=None):
-    """Copy the plan's active plane prefixes from pinned host tensors to device tensors."""
+def fathom_gather(planes_host, meta_host, depth, planes_dev, meta_dev, n=None, stream=None):
+    """Copy the plan's active plane prefixes (the first n tokens, default all
+    n_cap of a row) from pinned host tensors to device tensors."""
     G, d, four, nw = planes_host.shape
-    n = nw * 32
+    n_cap = nw * 32
+    n = n_cap if n is None else int(n)
     for t, nm in ((planes_host, "planes_host"), (meta_host, "meta_host")):
         if t.is_cuda or not t.is_pinned() or not t.is_contiguous():
             raise SDQError(f"{nm} must be a contiguous pinned host tensor")
-    if meta_host.numel() != G * d * (n // 64):
+    if meta_host.numel() != G * d * (n_cap // 64):
         raise SDQError("meta_host has the wrong size")
     _dev(depth, "depth", 1, G * d)
     _dev(planes_dev, "planes_dev", 4, planes_host.numel())
     _dev(meta_dev, "meta_dev", 4, meta_host.numel())
     _check(load().fathom_gather(_vp(planes_host.data_ptr()), _vp(meta_host.data_ptr()),
-                                _vp(depth.data_ptr()), G, d, n, _vp(planes_dev.data_ptr()),
+                                _vp(depth.data_ptr()), G, d, n, n_cap, _vp(planes_dev.data_ptr()),
                                 _vp(meta_dev.data_ptr()), _stream(stream)), "fathom_gather")
 
 
 def fathom_scan(index, depth, qbar, n, scores=None, block_max=None, planes=None, meta=None,
                 stream=None):
     """index: PlaneIndex (``planes``/``meta`` override its HBM buffers, e.g. a
-    staging copy filled by fathom_gather) -> scores float32 [G][n]; also fills
-    ``block_max`` float32 [G][n/64] if given."""
+    staging copy filled by fathom_gather); the first n tokens of its rows are
+    scored -> scores float32 [G][n64], n64 = n rounded up to 64 (tokens past n
+    score -inf); also fills ``block_max`` float32 [G][n64/64] if given."""
     G, d = depth.shape
     planes = index.planes if planes is None else planes
     meta = index.meta if meta is None else meta
-    _dev(planes, "planes", 4, G * d * 4 * (n // 32))
-    _dev(meta, "meta", 4, G * d * (n // 64))
+    n_cap = _index_sizes(planes, meta, G, d)
+    n64 = _round64(n)
     _dev(depth, "depth", 1, G * d)
     _dev(qbar, "qbar", 4, G * d)
-    scores = _out(scores, (G, n), torch.float32, planes.device, "scores", 4)
+    scores = _out(scores, (G, n64), torch.float32, planes.device, "scores", 4)
     bm = _vp(0)
     if block_max is not None:
-        bm = _dev(block_max, "block_max", 4, G * (n // 64))
+        bm = _dev(block_max, "block_max", 4, G * (n64 // 64))
     _check(load().fathom_scan(_vp(planes.data_ptr()), _vp(meta.data_ptr()), _vp(depth.data_ptr()),
-                              _vp(qbar.data_ptr()), G, d, n, _vp(scores.data_ptr()), bm,
+                              _vp(qbar.data_ptr()), G, d, int(n), n_cap, _vp(scores.data_ptr()), bm,
                               _stream(stream)), "fathom_scan")
     return scores
 
@@ -214,8 +271,8 @@ def fathom_plan_scan(index, q, key_var, budget_bits, n, depth=None, qbar=None, s
     meta = index.meta if meta is None else meta
     _dev(q, "q", 4, rows * d)
     _dev(key_var, "key_var", 4, G * d)
-    _dev(planes, "planes", 4, G * d * 4 * (n // 32))
-    _dev(meta, "meta", 4, G * d * (n // 64))
+    n_cap = _index_sizes(planes, meta, G, d)
+    n64 = _round64(n)
     if write_plan:
         depth = _out(depth, (G, d), torch.uint8, q.device, "depth", 1)
         qbar = _out(qbar, (G, d), torch.float32, q.device, "qbar", 4)
@@ -223,15 +280,15 @@ def fathom_plan_scan(index, q, key_var, budget_bits, n, depth=None, qbar=None, s
     else:
         depth = qbar = None
         dp = qp = _vp(0)
-    scores = _out(scores, (G, n), torch.float32, q.device, "scores", 4)
+    scores = _out(scores, (G, n64), torch.float32, q.device, "scores", 4)
     bm = _vp(0)
     if block_max is not None:
-        bm = _dev(block_max, "block_max", 4, G * (n // 64))
+        bm = _dev(block_max, "block_max", 4, G * (n64 // 64))
     uniform = uniform_channels is not None
     budget = int(uniform_channels) if uniform else int(budget_bits)
     _check(load().fathom_plan_scan(_vp(q.data_ptr()), _vp(key_var.data_ptr()), rows // G, budget,
                                    int(uniform), _vp(planes.data_ptr()), _vp(meta.data_ptr()), G, d,
-                                   n, dp, qp, _vp(scores.data_ptr()), bm, _stream(stream)),
+                                   int(n), n_cap, dp, qp, _vp(scores.data_ptr()), bm, _stream(stream)),
            "fathom_plan_scan")
     return depth, qbar, scores
 
@@ -277,29 +334,34 @@ def topk_select(keys, k, n_sink=0, n_local=0, idx=None, ws=None, stream=None):
     return idx
 
 
-def hamming_scan(sigs, qsig, dist=None, stream=None):
-    """sigs uint32 [H][n], qsig uint32 [H] -> dist uint8 [H][n]."""
-    H, n = sigs.shape
-    _dev(sigs, "sigs", 4, H * n)
+def hamming_scan(sigs, qsig, dist=None, n=None, stream=None):
+    """sigs uint32 [H][n_cap] (the first n scored, default all), qsig uint32 [H]
+    -> dist uint8 [H][n]."""
+    H, n_cap = sigs.shape
+    n = n_cap if n is None else int(n)
+    _dev(sigs, "sigs", 4, H * n_cap)
     _dev(qsig, "qsig", 4, H)
     dist = _out(dist, (H, n), torch.uint8, sigs.device, "dist", 1)
-    _check(load().hamming_scan(_vp(sigs.data_ptr()), _vp(qsig.data_ptr()), H, n,
+    _check(load().hamming_scan(_vp(sigs.data_ptr()), _vp(qsig.data_ptr()), H, n, n_cap,
                                _vp(dist.data_ptr()), _stream(stream)), "hamming_scan")
     return dist
 
 
-def minmax_block_scan(bmin, bmax, q, scores=None, stream=None):
-    """bmin, bmax fp16 bits [RG][nb][128], q float32 [RG*H_grp][128] -> scores float32 [RG][nb]."""
-    RG, nb, d = bmin.shape
-    _dev(bmin, "bmin", 2, RG * nb * d)
-    _dev(bmax, "bmax", 2, RG * nb * d)
+def minmax_block_scan(bmin, bmax, q, scores=None, nb=None, stream=None):
+    """bmin, bmax fp16 bits [RG][nb_cap][128] (the first nb blocks scored,
+    default all), q float32 [RG*H_grp][128] -> scores float32 [RG][nb]."""
+    RG, nb_cap, d = bmin.shape
+    nb = nb_cap if nb is None else int(nb)
+    _dev(bmin, "bmin", 2, RG * nb_cap * d)
+    _dev(bmax, "bmax", 2, RG * nb_cap * d)
     rows = q.numel() // d
     if rows % RG:
         raise SDQError("q rows must be a multiple of RG")
     _dev(q, "q", 4, rows * d)
     scores = _out(scores, (RG, nb), torch.float32, bmin.device, "scores", 4)
     _check(load().minmax_block_scan(_vp(bmin.data_ptr()), _vp(bmax.data_ptr()), _vp(q.data_ptr()),
-                                    RG, rows // RG, nb, d, _vp(scores.data_ptr()), _stream(stream)),
+                                    RG, rows // RG, nb, nb_cap, d, _vp(scores.data_ptr()),
+                                    _stream(stream)),
            "minmax_block_scan")
     return scores
 
@@ -311,17 +373,18 @@ def attend_workspace(R, Hq, Hkv, per_query_head, n_idx, block_tokens, device="cu
 
 
 def gather_attend_host_kv(q, K_host, V_host, idx, block_tokens=1, per_query_head=False,
-                          softmax_scale=None, out=None, ws=None, stream=None):
+                          softmax_scale=None, out=None, ws=None, n=None, stream=None):
     """As gather_attend, with K and V pinned host tensors (bf16 bits as int16/uint16)
     read in place over the host link."""
     R, Hq, d = q.shape
-    _, Hkv, n, _ = K_host.shape
+    _, Hkv, n_cap, _ = K_host.shape
+    n = n_cap if n is None else int(n)
     n_idx = idx.shape[-1]
     Hsel = Hq if per_query_head else Hkv
     for t, nm in ((K_host, "K_host"), (V_host, "V_host")):
         if t.is_cuda or not t.is_pinned() or not t.is_contiguous() or t.element_size() != 2:
             raise SDQError(f"{nm} must be a contiguous pinned host tensor of 2-byte elements")
-        if t.numel() != R * Hkv * n * d:
+        if t.numel() != R * Hkv * n_cap * d:
             raise SDQError(f"{nm} has the wrong size")
     _dev(q, "q", 4, R * Hq * d)
     _dev(idx, "idx", 4, R * Hsel * n_idx)
@@ -332,23 +395,24 @@ def gather_attend_host_kv(q, K_host, V_host, idx, block_tokens=1, per_query_head
     scale = (1.0 / d ** 0.5) if softmax_scale is None else float(softmax_scale)
     _check(load().gather_attend_host_kv(_vp(q.data_ptr()), _vp(K_host.data_ptr()),
                                         _vp(V_host.data_ptr()), _vp(idx.data_ptr()), R, Hq, Hkv,
-                                        int(bool(per_query_head)), n, n_idx, int(block_tokens), d,
+                                        int(bool(per_query_head)), n, n_cap, n_idx, int(block_tokens), d,
                                         scale, _vp(out.data_ptr()), _vp(ws.data_ptr()), ws.numel(),
                                         _stream(stream)), "gather_attend_host_kv")
     return out
 
 
 def gather_attend(q, K, V, idx, block_tokens=1, per_query_head=False, softmax_scale=None,
-                  out=None, ws=None, stream=None):
-    """q float32 [R][Hq][128]; K, V bf16 [R][Hkv][n][128]; idx int32 [R][Hsel][n_idx]
-    -> out float32 [R][Hq][128]."""
+                  out=None, ws=None, n=None, stream=None):
+    """q float32 [R][Hq][128]; K, V bf16 [R][Hkv][n_cap][128] with the first n
+    rows valid (default all); idx int32 [R][Hsel][n_idx] -> out float32 [R][Hq][128]."""
     R, Hq, d = q.shape
-    _, Hkv, n, _ = K.shape
+    _, Hkv, n_cap, _ = K.shape
+    n = n_cap if n is None else int(n)
     n_idx = idx.shape[-1]
     Hsel = Hq if per_query_head else Hkv
     _dev(q, "q", 4, R * Hq * d)
-    _dev(K, "K", 2, R * Hkv * n * d)
-    _dev(V, "V", 2, R * Hkv * n * d)
+    _dev(K, "K", 2, R * Hkv * n_cap * d)
+    _dev(V, "V", 2, R * Hkv * n_cap * d)
     _dev(idx, "idx", 4, R * Hsel * n_idx)
     out = _out(out, (R, Hq, d), torch.float32, q.device, "out", 4)
     if ws is None:
@@ -356,7 +420,7 @@ def gather_attend(q, K, V, idx, block_tokens=1, per_query_head=False, softmax_sc
     _dev(ws, "ws", 1)
     scale = (1.0 / d ** 0.5) if softmax_scale is None else float(softmax_scale)
     _check(load().gather_attend(_vp(q.data_ptr()), _vp(K.data_ptr()), _vp(V.data_ptr()),
-                                _vp(idx.data_ptr()), R, Hq, Hkv, int(bool(per_query_head)), n, n_idx,
+                                _vp(idx.data_ptr()), R, Hq, Hkv, int(bool(per_query_head)), n, n_cap, n_idx,
                                 int(block_tokens), d, scale, _vp(out.data_ptr()), _vp(ws.data_ptr()),
                                 ws.numel(), _stream(stream)), "gather_attend")
     return out

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     L = sdq.load()
     for name in _declared():
         assert hasattr(L, name), name
-    assert L.sdq_abi_version() == 1
+    assert L.sdq_abi_version() == 2
 
 
 def test_invalid_arguments_rejected_without_launch():
@@ -39,24 +39,41 @@ def test_invalid_arguments_rejected_without_launch():
     null = ctypes.c_void_p(0)
     s = ctypes.c_void_p(0)
     EINVAL = -1
-    assert L.fathom_scan(null, p, p, p, 8, 128, 4096, p, null, s) == EINVAL
+    assert L.fathom_scan(null, p, p, p, 8, 128, 4096, 4096, p, null, s) == EINVAL
     assert b"null" in L.sdq_last_error()
-    assert L.fathom_scan(p, p, p, p, 8, 128, 4000, p, null, s) == EINVAL    # n % 64
-    assert L.fathom_scan(p, p, p, p, 8, 64, 4096, p, null, s) == EINVAL     # d != 128
+    assert L.fathom_scan(p, p, p, p, 8, 128, 4096, 4000, p, null, s) == EINVAL   # n_cap % 64
+    assert L.fathom_scan(p, p, p, p, 8, 128, 4097, 4096, p, null, s) == EINVAL   # n > n_cap
+    assert L.fathom_scan(p, p, p, p, 8, 128, 0, 4096, p, null, s) == EINVAL      # n < 1
+    assert L.fathom_scan(p, p, p, p, 8, 128, 64, 1 << 25, p, null, s) == EINVAL  # n_cap >= 2^25
+    assert L.fathom_scan(p, p, p, p, 8, 64, 4096, 4096, p, null, s) == EINVAL    # d != 128
+    assert L.fathom_scan(p, p, p, p, 8, 128, 4096, 4096, ctypes.c_void_p(0x1004), null, s) == EINVAL  # align
     assert L.fathom_plan(p, p, 8, 4, 128, -1, p, p, s) == EINVAL             # negative budget
-    assert L.fathom_plan_scan(p, p, 4, 56, 0, p, p, 8, 128, 4096, p, null, p, null, s) == EINVAL  # depth only
-    assert L.fathom_plan_scan(p, p, 4, 56, 0, p, p, 8, 128, 4000, null, null, p, null, s) == EINVAL  # n % 64
-    assert L.fathom_plan_scan(p, p, 4, 129, 1, p, p, 8, 128, 4096, null, null, p, null, s) == EINVAL  # > d channels
+    assert L.fathom_plan_scan(p, p, 4, 56, 0, p, p, 8, 128, 4096, 4096, p, null, p, null, s) == EINVAL  # depth only
+    assert L.fathom_plan_scan(p, p, 4, 56, 0, p, p, 8, 128, 4096, 4000, null, null, p, null, s) == EINVAL  # n_cap % 64
+    assert L.fathom_plan_scan(p, p, 4, 129, 1, p, p, 8, 128, 4096, 4096, null, null, p, null, s) == EINVAL  # > d channels
     assert L.fathom_plan_uniform(p, p, 8, 4, 128, 129, p, p, s) == EINVAL    # > d channels
     assert L.fathom_ingest(p, 0, 4096, 128, p, p, s) == EINVAL               # G < 1
+    assert L.fathom_append(p, 8, 128, 4096, 4000, 97, p, p, s) == EINVAL     # past n_cap
+    assert L.fathom_append(p, 8, 128, 4000, 0, 1, p, p, s) == EINVAL         # n_cap % 64
+    assert L.fathom_append(p, 8, 128, 4096, -1, 1, p, p, s) == EINVAL        # n_old < 0
+    assert L.fathom_append(null, 8, 128, 4096, 0, 1, p, p, s) == EINVAL
+    assert L.fathom_append(p, 8, 128, 4096, 100, 0, p, p, s) == 0            # nothing to do
+    assert L.minmax_append(p, 8, 128, 4096, 0, 1, 0, p, p, s) == EINVAL      # block < 1
+    assert L.minmax_append(p, 8, 128, 4001, 0, 1, 16, p, p, s) == EINVAL     # n_cap % block
+    assert L.minmax_append(p, 8, 128, 4096, 4096, 1, 16, p, p, s) == EINVAL  # past n_cap
+    assert L.fathom_gather(p, p, p, 8, 128, 4097, 4096, p, p, s) == EINVAL   # n > n_cap
     assert L.topk_select(p, 7, 1, 10, 2, 0, 0, p, p, 256, s) == EINVAL       # key type
     assert L.topk_select(p, 0, 1, 10, 2, 6, 5, p, p, 256, s) == EINVAL       # windows > n
     assert L.topk_select(p, 0, 8, 1 << 20, 512, 0, 0, p, null, 0, s) == EINVAL   # no workspace
-    assert L.hamming_scan(p, p, 0, 10, p, s) == EINVAL
-    assert L.minmax_block_scan(p, p, p, 1, 4, 0, 128, p, s) == EINVAL
-    assert L.gather_attend(p, p, p, p, 1, 32, 6, 0, 100, 8, 1, 128, 1.0, p, p, 1 << 20, s) == EINVAL
-    assert L.gather_attend(p, p, p, p, 1, 32, 8, 0, 2000, 1024, 1, 128, 1.0, p, p, 0, s) == EINVAL  # ws
-    assert L.gather_attend(p, p, p, p, 1, 32, 8, 0, 1 << 23, 512, 1, 128, 1.0, p, p, 1 << 20, s) == EINVAL
+    assert L.hamming_scan(p, p, 0, 10, 10, p, s) == EINVAL
+    assert L.hamming_scan(p, p, 4, 11, 10, p, s) == EINVAL                   # n > n_cap
+    assert L.minmax_block_scan(p, p, p, 1, 4, 0, 8, 128, p, s) == EINVAL
+    assert L.minmax_block_scan(p, p, p, 1, 4, 9, 8, 128, p, s) == EINVAL     # nb > nb_cap
+    assert L.gather_attend(p, p, p, p, 1, 32, 6, 0, 100, 100, 8, 1, 128, 1.0, p, p, 1 << 20, s) == EINVAL
+    assert L.gather_attend(p, p, p, p, 1, 32, 8, 0, 2000, 2000, 1024, 1, 128, 1.0, p, p, 0, s) == EINVAL  # ws
+    assert L.gather_attend(p, p, p, p, 1, 32, 8, 0, 1 << 23, 1 << 23, 512, 1, 128, 1.0, p, p, 1 << 20,
+                           s) == EINVAL
+    assert L.gather_attend(p, p, p, p, 1, 32, 8, 0, 2001, 2000, 8, 1, 128, 1.0, p, p, 1 << 20, s) == EINVAL
 
 
 def test_workspace_sizes():
