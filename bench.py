@@ -324,11 +324,17 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def timeit(torch, fn, reps=30, warm=3):
+def timeit(torch, fn, reps=30, warm=3, cover=None):
+    """Mean GPU time per call between two events.  For calls shorter than
+    their host-side launch cost, ``cover`` (a callable) first queues a long
+    GPU operation, so that every timed call is already queued when the first
+    one starts and the events measure the calls back to back."""
     for i in range(warm):
         fn(i)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if cover is not None:
+        cover()
     e0.record()
     for i in range(reps):
         fn(i)
@@ -395,6 +401,43 @@ def run_extras(torch, np, lib, bytemodel, synth, dev, case, K4, V4, q, var, q3, 
                                  "device_resident_us": round(us_dev, 1)}
     log(f"extras: host K/V attention {us:.0f} us")
     del Kh, Vh
+
+    # decode-time appends into this layer's cache (rows of n tokens): the new
+    # tokens' blocks are quantised again; appending keys already there
+    # rewrites the same words, so the index stays as it was
+    # (one append is a few microseconds of GPU work but about ten of host-side
+    # launch cost, so a 2 GiB multiply is queued ahead of the timed calls)
+    big = torch.ones(1 << 29, device=dev)
+    cover = lambda: big.mul_(1.0)                                   # noqa: E731
+    for m in (1, 64):
+        us = timeit(torch, lambda i: lib.fathom_append(K4[0], n - m, m, index), reps=30, warm=5,
+                    cover=cover)
+        ex[f"fathom_append_{m}tok_us"] = round(us, 2)
+    bmin_a = torch.empty(G, n // 16, 128, dtype=torch.int16, device=dev)
+    bmax_a = torch.empty_like(bmin_a)
+    us = timeit(torch, lambda i: lib.minmax_append(K4[0], n - 1, 1, bmin_a, bmax_a, 16), reps=30,
+                warm=5, cover=cover)
+    ex["minmax_append_1tok_us"] = round(us, 2)
+    del bmin_a, bmax_a, big
+    log(f"extras: append {ex['fathom_append_1tok_us']} us (1 token), {ex['fathom_append_64tok_us']} us (64)")
+
+    # a whole step at a ragged length (the open block's last 27 slots empty),
+    # the last 64 positions kept as the local window
+    n_r = n - 27
+    sc_r = torch.empty(G, n, device=dev)
+    bm_r = torch.empty(G, n // 64, device=dev)
+    idx_r = torch.empty(G, k + 64, dtype=torch.int32, device=dev)
+    ws_r = lib.attend_workspace(1, G * Hgrp, G, False, k + 64, 1, dev)
+    out_r = torch.empty_like(q3)
+
+    def ragged(i):
+        lib.fathom_plan_scan(index, q, var, 56, n_r, planes=P[i % len(P)], meta=M[i % len(M)],
+                             scores=sc_r, block_max=bm_r, write_plan=False)
+        lib.topk_select_block_max(sc_r, bm_r, k, n_local=64, idx=idx_r)
+        lib.gather_attend(q3, K4, V4, idx_r.view(1, G, -1), out=out_r, ws=ws_r, n=n_r)
+    ex["decode_step_ragged_us"] = round(timeit(torch, ragged), 2)
+    log(f"extras: ragged step {ex['decode_step_ragged_us']} us")
+    del sc_r, bm_r, idx_r, ws_r, out_r
 
     # read-plan quality on this layer: sparse vs dense attention error, needle and
     # exact top-k recall, scan bytes per plan

@@ -75,9 +75,10 @@ int sdq_abi_version(void);
  *           fp16 offset of that channel's 64-token block.
  * Quantiser (float32): offset = fp16(min), scale = fp16((max-min)/15),
  * code = clamp(rint((x - offset)/scale), 0, 15), code 0 where scale is 0.
- * Keys must be finite and within fp16 range.
- * Errors: SDQ_EINVAL if a pointer is null, G < 1, n < 64, n % 64 != 0 or
- * d != 128. */
+ * Keys must be finite and within fp16 range; the key pointer must be 16-byte
+ * aligned.
+ * Errors: SDQ_EINVAL if a pointer is null or keys misaligned, G < 1, n < 64,
+ * n % 64 != 0 or d != 128. */
 int fathom_ingest(const uint16_t* keys, int G, int n, int d, uint32_t* planes, uint32_t* meta,
                   hipStream_t stream);
 
@@ -96,8 +97,9 @@ int fathom_ingest(const uint16_t* keys, int G, int n, int d, uint32_t* planes, u
  *           last touched block are left as they are.
  *   meta    uint32 [G][d][n_cap/64]  in/out, likewise.
  * n_new == 0 is a no-op.
- * Errors: SDQ_EINVAL on null pointers, G < 1, d != 128, n_cap not a positive
- * multiple of 64 below 2^25, n_old < 0, n_new < 0, n_old + n_new > n_cap. */
+ * Errors: SDQ_EINVAL on null pointers, keys not 16-byte aligned, G < 1,
+ * d != 128, n_cap not a positive multiple of 64 below 2^25, n_old < 0,
+ * n_new < 0, n_old + n_new > n_cap. */
 int fathom_append(const uint16_t* keys, int G, int d, int n_cap, int n_old, int n_new,
                   uint32_t* planes, uint32_t* meta, hipStream_t stream);
 

@@ -11,70 +11,76 @@
 
 namespace sdq {
 
-// One thread owns a pair of adjacent channels; the 64 threads of a wave cover
-// the 128 channels, so each token row (256 bytes) is read by one coalesced
-// 4-byte-per-lane load.  A workgroup walks `bpw` consecutive 64-token blocks
-// of the range [b0, b0 + nblk).
+// One workgroup of 256 threads per (KV head, 64-token block).  The block's
+// 64 key rows (16 KB) come in as coalesced 16-byte loads and are staged in
+// LDS; thread (j, h) then takes channel j: the min and max over the block's
+// 64 rows, then the codes of tokens 32h..32h+31, i.e. one word of each of the
+// four planes.  A workgroup covers blocks [b0, b0 + nblk) of one head along
+// gridDim.x.
 //
 // Rows are n_cap tokens long (the cache's capacity) and the first n tokens
 // are present.  A partly filled last block (the open block of a growing
-// cache) is quantised over its m present tokens: loads past them repeat the
-// last present row, which leaves the block's min and max unchanged, and the
-// absent tokens' plane bits are cleared.
-__global__ __launch_bounds__(64) void fathom_append_kernel(const uint32_t* __restrict__ keys,
-                                                           int n_cap, int n, int b0, int nblk,
-                                                           int bpw, uint32_t* __restrict__ planes,
-                                                           uint32_t* __restrict__ meta) {
+// cache) is quantised over its m present tokens: rows past them are staged as
+// copies of the last present row, which leaves the block's min and max
+// unchanged, and the absent tokens' plane bits are cleared.
+constexpr int kApThreads = 256;
+
+__global__ __launch_bounds__(kApThreads) void fathom_append_kernel(
+    const uint4* __restrict__ keys, int n_cap, int n, int b0, uint32_t* __restrict__ planes,
+    uint32_t* __restrict__ meta) {
+  __shared__ uint16_t s_k[64][kHeadDim];
   const int g = blockIdx.y;
-  const int pair = threadIdx.x;
-  const size_t nw = size_t(n_cap) / 32;                   // 32-token words per plane row
-  const int nb_cap = n_cap / 64;
-  for (int bb = 0; bb < bpw; ++bb) {
-    const int bi = blockIdx.x * bpw + bb;
-    if (bi >= nblk) break;
-    const int b = b0 + bi;
-    const int m = n - b * 64 < 64 ? n - b * 64 : 64;       // present tokens, >= 1
-    const uint32_t* src = keys + (size_t(g) * n_cap + size_t(b) * 64) * (kHeadDim / 2) + pair;
-    uint32_t w[64];
+  const int b = b0 + blockIdx.x;
+  const int t = threadIdx.x;
+  const int m = n - b * 64 < 64 ? n - b * 64 : 64;          // present tokens, >= 1
+  const uint4* src = keys + (size_t(g) * n_cap + size_t(b) * 64) * (kHeadDim / 8);
+  uint4 v[4];
 #pragma unroll
-    for (int i = 0; i < 64; ++i) w[i] = src[size_t(i < m ? i : m - 1) * (kHeadDim / 2)];
-    const uint32_t keep0 = m >= 32 ? 0xFFFFFFFFu : (1u << m) - 1u;
-    const uint32_t keep1 = m >= 64 ? 0xFFFFFFFFu : (m > 32 ? (1u << (m - 32)) - 1u : 0u);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      float mn = INFINITY, mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 64; ++i) {
-        const float x = half ? bf16_hi(w[i]) : bf16_lo(w[i]);
-        mn = fminf(mn, x);
-        mx = fmaxf(mx, x);
-      }
-      const _Float16 off16 = _Float16(mn);
-      const _Float16 sc16 = _Float16(__fdiv_rn(mx - mn, 15.0f));
-      const float off = float(off16);
-      const float sc = float(sc16);
-      uint32_t pl[4][2] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
-#pragma unroll
-      for (int i = 0; i < 64; ++i) {
-        const float x = half ? bf16_hi(w[i]) : bf16_lo(w[i]);
-        float r = (sc == 0.0f) ? 0.0f : rintf(__fdiv_rn(x - off, sc));
-        r = fminf(fmaxf(r, 0.0f), 15.0f);
-        const uint32_t code = uint32_t(r);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) pl[p][i >> 5] |= ((code >> (3 - p)) & 1u) << (i & 31);
-      }
-      const int j = 2 * pair + half;
-      uint32_t* prow = planes + (size_t(g) * kHeadDim + j) * 4 * nw;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        prow[size_t(p) * nw + 2 * size_t(b)] = pl[p][0] & keep0;
-        prow[size_t(p) * nw + 2 * size_t(b) + 1] = pl[p][1] & keep1;
-      }
-      meta[(size_t(g) * kHeadDim + j) * nb_cap + b] =
-          uint32_t(__builtin_bit_cast(uint16_t, sc16)) |
-          (uint32_t(__builtin_bit_cast(uint16_t, off16)) << 16);
-    }
+  for (int e = 0; e < 4; ++e) {                              // 1024 16-byte pieces, 4 per thread
+    const int f = e * kApThreads + t;
+    const int row = f >> 4;
+    v[e] = src[size_t(row < m ? row : m - 1) * (kHeadDim / 8) + (f & 15)];
   }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int f = e * kApThreads + t;
+    reinterpret_cast<uint4*>(&s_k[f >> 4][0])[f & 15] = v[e];
+  }
+  __syncthreads();
+
+  const int j = t & (kHeadDim - 1);
+  const int h = t >> 7;                                      // which 32-token half
+  float mn = INFINITY, mx = -INFINITY;
+#pragma unroll 16
+  for (int i = 0; i < 64; ++i) {
+    const float x = __uint_as_float(uint32_t(s_k[i][j]) << 16);
+    mn = fminf(mn, x);
+    mx = fmaxf(mx, x);
+  }
+  const _Float16 off16 = _Float16(mn);
+  const _Float16 sc16 = _Float16(__fdiv_rn(mx - mn, 15.0f));
+  const float off = float(off16);
+  const float sc = float(sc16);
+  uint32_t pl[4] = {0, 0, 0, 0};
+#pragma unroll 8
+  for (int i = 0; i < 32; ++i) {
+    const float x = __uint_as_float(uint32_t(s_k[32 * h + i][j]) << 16);
+    float r = (sc == 0.0f) ? 0.0f : rintf(__fdiv_rn(x - off, sc));
+    r = fminf(fmaxf(r, 0.0f), 15.0f);
+    const uint32_t code = uint32_t(r);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) pl[p] |= ((code >> (3 - p)) & 1u) << i;
+  }
+  const int mh = m - 32 * h;                                 // present tokens of this half
+  const uint32_t keep = mh >= 32 ? 0xFFFFFFFFu : (mh > 0 ? (1u << mh) - 1u : 0u);
+  const size_t nw = size_t(n_cap) / 32;                      // 32-token words per plane row
+  uint32_t* prow = planes + (size_t(g) * kHeadDim + j) * 4 * nw + 2 * size_t(b) + h;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) prow[size_t(p) * nw] = pl[p] & keep;
+  if (h == 0)
+    meta[(size_t(g) * kHeadDim + j) * (n_cap / 64) + b] =
+        uint32_t(__builtin_bit_cast(uint16_t, sc16)) |
+        (uint32_t(__builtin_bit_cast(uint16_t, off16)) << 16);
 }
 
 __device__ __forceinline__ uint32_t f16_next_down(uint32_t h) {
@@ -114,13 +120,21 @@ __global__ __launch_bounds__(64) void minmax_append_kernel(const uint32_t* __res
     const int m = n - b * block < block ? n - b * block : block;
     const uint32_t* src = keys + (size_t(rg) * n_cap + size_t(b) * block) * (kHeadDim / 2) + pair;
     float lo0 = INFINITY, lo1 = INFINITY, hi0 = -INFINITY, hi1 = -INFINITY;
-    for (int i = 0; i < m; ++i) {
-      const uint32_t w = src[size_t(i) * (kHeadDim / 2)];
-      const float a = bf16_lo(w), c = bf16_hi(w);
-      lo0 = fminf(lo0, a);
-      hi0 = fmaxf(hi0, a);
-      lo1 = fminf(lo1, c);
-      hi1 = fmaxf(hi1, c);
+    // rows in batches of 16, every load of a batch issued before the first
+    // use; rows past m repeat row m - 1, which leaves min and max unchanged
+    for (int i0 = 0; i0 < m; i0 += 16) {
+      uint32_t w[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        w[u] = src[size_t(i0 + u < m ? i0 + u : m - 1) * (kHeadDim / 2)];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const float a = bf16_lo(w[u]), c = bf16_hi(w[u]);
+        lo0 = fminf(lo0, a);
+        hi0 = fmaxf(hi0, a);
+        lo1 = fminf(lo1, c);
+        hi1 = fmaxf(hi1, c);
+      }
     }
     const size_t o = (size_t(rg) * nb_cap + b) * (kHeadDim / 2) + pair;
     bmin[o] = f16_round_down(lo0) | (f16_round_down(lo1) << 16);
@@ -134,10 +148,9 @@ using namespace sdq;
 
 static void launch_fathom_append(const uint16_t* keys, int G, int n_cap, int n, int b0, int nblk,
                                  uint32_t* planes, uint32_t* meta, hipStream_t stream) {
-  const int bpw = 4;
-  dim3 grid(cdiv(nblk, bpw), G);
-  hipLaunchKernelGGL(fathom_append_kernel, grid, dim3(64), 0, stream,
-                     reinterpret_cast<const uint32_t*>(keys), n_cap, n, b0, nblk, bpw, planes, meta);
+  dim3 grid(nblk, G);
+  hipLaunchKernelGGL(fathom_append_kernel, grid, dim3(kApThreads), 0, stream,
+                     reinterpret_cast<const uint4*>(keys), n_cap, n, b0, planes, meta);
 }
 
 extern "C" int fathom_ingest(const uint16_t* keys, int G, int n, int d, uint32_t* planes,
@@ -147,6 +160,7 @@ extern "C" int fathom_ingest(const uint16_t* keys, int G, int n, int d, uint32_t
   SDQ_REQUIRE(n >= 64 && n % 64 == 0, "fathom_ingest: n=%d must be a positive multiple of 64", n);
   SDQ_REQUIRE(n < (1 << 25), "fathom_ingest: n=%d must be below 2^25", n);
   SDQ_REQUIRE(d == kHeadDim, "fathom_ingest: d=%d unsupported (only 128)", d);
+  SDQ_REQUIRE(reinterpret_cast<uintptr_t>(keys) % 16 == 0, "fathom_ingest: keys must be 16-byte aligned");
   launch_fathom_append(keys, G, n, n, 0, n / 64, planes, meta, stream);
   return check_launch("fathom_ingest");
 }
@@ -156,6 +170,7 @@ extern "C" int fathom_append(const uint16_t* keys, int G, int d, int n_cap, int 
   SDQ_REQUIRE(keys && planes && meta, "fathom_append: null pointer");
   SDQ_REQUIRE(G >= 1, "fathom_append: G=%d must be >= 1", G);
   SDQ_REQUIRE(d == kHeadDim, "fathom_append: d=%d unsupported (only 128)", d);
+  SDQ_REQUIRE(reinterpret_cast<uintptr_t>(keys) % 16 == 0, "fathom_append: keys must be 16-byte aligned");
   SDQ_REQUIRE(n_cap >= 64 && n_cap % 64 == 0 && n_cap < (1 << 25),
               "fathom_append: n_cap=%d must be a positive multiple of 64 below 2^25", n_cap);
   SDQ_REQUIRE(n_old >= 0 && n_new >= 0 && (long long)n_old + n_new <= n_cap,

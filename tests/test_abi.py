@@ -57,6 +57,7 @@ def test_invalid_arguments_rejected_without_launch():
     assert L.fathom_append(p, 8, 128, 4000, 0, 1, p, p, s) == EINVAL         # n_cap % 64
     assert L.fathom_append(p, 8, 128, 4096, -1, 1, p, p, s) == EINVAL        # n_old < 0
     assert L.fathom_append(null, 8, 128, 4096, 0, 1, p, p, s) == EINVAL
+    assert L.fathom_append(ctypes.c_void_p(0x1008), 8, 128, 4096, 0, 1, p, p, s) == EINVAL  # align
     assert L.fathom_append(p, 8, 128, 4096, 100, 0, p, p, s) == 0            # nothing to do
     assert L.minmax_append(p, 8, 128, 4096, 0, 1, 0, p, p, s) == EINVAL      # block < 1
     assert L.minmax_append(p, 8, 128, 4001, 0, 1, 16, p, p, s) == EINVAL     # n_cap % block
