@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from oracle import fathom, select, hamming, quest, attend
+from oracle import fathom, select, hamming, quest, attend, oasis
 import synth
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -517,3 +517,79 @@ def test_byte_model_against_pages():
     # the plane scan's read bytes for the uniform plan equal 17 B per token
     dep = [[4] * 34 + [0] * 94]
     assert bm.plane_scan_read_bytes(1 << 20, dep) == (1 << 20) * (136 // 8) + 34 * (1 << 14) * 4
+
+
+# ---------------------------------------------------------------- KV selection (resident pool)
+def test_oasis_select_worked_example():
+    rec = _read_golden("oasis_select_example.txt")
+    resident = [int(x) for x in rec["resident"]]
+    last_sel = [int(x) for x in rec["last_sel"]]
+    step = int(rec["step"][0])
+    pred = [int(x) for x in rec["pred"]]
+    scores = np.zeros(16)
+    for line in open(os.path.join(GOLDEN, "oasis_select_example.txt")):
+        if line.startswith("score_block"):
+            _, b, v = line.split()
+            scores[int(b)] = float(v)
+    for cap in (2, 1):
+        res, ls, plan = oasis.select(pred, scores, resident, last_sel, step, cap)
+        assert res == [int(x) for x in rec[f"cap{cap}_resident"]]
+        assert ls == [int(x) for x in rec[f"cap{cap}_last_sel"]]
+        assert plan == [tuple(int(v) for v in e.split(":")) for e in rec[f"cap{cap}_plan"]]
+
+
+def test_oasis_select_invariants():
+    """Random pools: the plan has min(C, misses, targets) pairs; hits stay;
+    evicted blocks were never predicted; the pool's blocks stay distinct; an
+    evicted occupied slot is never more recently selected than a kept
+    unpredicted one; with enough cap and targets every predicted block ends
+    up resident."""
+    g = np.random.default_rng(71)
+    for trial in range(300):
+        nb = int(g.integers(4, 60))
+        S = int(g.integers(1, min(nb, 24) + 1))
+        occ = g.choice(nb, size=int(g.integers(0, S + 1)), replace=False)
+        resident = np.full(S, -1)
+        resident[g.choice(S, size=len(occ), replace=False)] = occ
+        last_sel = g.integers(0, 5, size=S)          # many equal stamps
+        K = int(g.integers(0, min(nb, 30) + 1))
+        pred = g.choice(nb, size=K, replace=False)
+        scores = g.integers(0, 4, size=nb).astype(float)   # many equal scores
+        cap = int(g.integers(0, 8))
+        step = 9
+        res, ls, plan = oasis.select(pred, scores, resident, last_sel, step, cap)
+        P, held = set(pred.tolist()), set(resident[resident >= 0].tolist())
+        misses = P - held
+        targets = [s for s in range(S) if resident[s] < 0 or resident[s] not in P]
+        assert len(plan) == min(cap, len(misses), len(targets))
+        after = [b for b in res if b >= 0]
+        assert len(after) == len(set(after))
+        for s in range(S):
+            if resident[s] >= 0 and resident[s] in P:
+                assert res[s] == resident[s] and ls[s] == step
+        evicted = {s for s, _ in plan}
+        for s in evicted:
+            assert resident[s] < 0 or resident[s] not in P
+        kept_unpred = [s for s in targets if s not in evicted]
+        for s in evicted:
+            for t in kept_unpred:
+                if resident[s] >= 0 and resident[t] >= 0:
+                    assert (last_sel[s], s) < (last_sel[t], t)
+                if resident[t] < 0:
+                    assert resident[s] < 0 and s < t      # empty slots go first
+        fetched = [b for _, b in plan]
+        if fetched:
+            # the fetched misses are the best ones
+            worst = max((-scores[b], b) for b in fetched)
+            for b in misses - set(fetched):
+                assert (-scores[b], b) > worst
+        if cap >= len(misses) and len(targets) >= len(misses):
+            assert P <= set(after)
+
+
+def test_oasis_fetch_copies_planned_blocks():
+    pool = np.zeros((4, 2, 3))
+    host = np.arange(10 * 6, dtype=float).reshape(10, 2, 3)
+    out = oasis.fetch(pool, host, [(1, 6), (3, 4)])
+    assert np.array_equal(out[1], host[6]) and np.array_equal(out[3], host[4])
+    assert not out[0].any() and not out[2].any()
