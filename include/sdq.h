@@ -55,7 +55,8 @@ const char* sdq_last_error(void);
 
 /* ABI version of this header (incremented on incompatible changes).
  * Version 2: row capacities (n_cap, nb_cap) on every call that reads
- * per-token cache arrays; fathom_append and minmax_append. */
+ * per-token cache arrays; fathom_append, minmax_append, oasis_select and
+ * oasis_fetch. */
 int sdq_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -322,6 +323,53 @@ int gather_attend_host_kv(const float* q, const uint16_t* K_host, const uint16_t
                           int n, int n_cap, int n_idx, int block_tokens, int d,
                           float softmax_scale, float* out, void* ws, size_t ws_bytes,
                           hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Resident block pool (OasisKV review, core method and method steps)
+ * --------------------------------------------------------------------- */
+
+/* oasis_select -- KV selection of one step against a GPU-resident pool.
+ * For every row r (a request's KV head): the predicted blocks P = pred[r]
+ * are intersected with the pool resident[r] (S slots, block id or -1 for an
+ * empty slot).  Hits keep their slot and get last_sel = step.  Predicted
+ * blocks that are not resident (misses) are ordered by block_scores[r]
+ * descending, equal scores to the lower block id; eviction targets (slots
+ * whose block is not in P) are ordered empty slots first, then by last_sel
+ * ascending, equal stamps to the lower slot.  The i-th miss is paired with the
+ * i-th target for i < min(cap, misses, targets): the slot takes the block and
+ * last_sel = step.
+ *   pred          int32 [rows][K]  distinct block ids; entries outside
+ *                 [0, nb) are ignored
+ *   block_scores  float32 [rows][nb], not NaN
+ *   resident, last_sel  int32 [rows][S]  in/out
+ *   plan_slot, plan_block  int32 [rows][cap] out: the pairs in order, -1
+ *                 padded (the transfer plan of oasis_fetch)
+ *   n_fetch       int32 [rows] out: pairs made
+ *   slots_out     int32 [rows][S] out, or NULL: s for every slot that holds a
+ *                 block after the step, -1 otherwise (the index set of
+ *                 gather_attend over the pool, in block units)
+ * Limits: K <= 1024, S <= 1024, cap <= 1024, nb <= 65536.
+ * Errors: SDQ_EINVAL on null pointers (pred and block_scores may be NULL when
+ * K == 0, the plan when cap == 0), rows < 1 and the limits above. */
+int oasis_select(const int32_t* pred, int K, const float* block_scores, int nb, int rows,
+                 int32_t* resident, int32_t* last_sel, int S, int step, int cap,
+                 int32_t* plan_slot, int32_t* plan_block, int32_t* n_fetch, int32_t* slots_out,
+                 hipStream_t stream);
+
+/* oasis_fetch -- carry out a transfer plan: block plan_block[r][i] of row r's
+ * host cache is copied into slot plan_slot[r][i] of row r's pool, for both K
+ * and V, read in place over the host link (OasisKV review: a UVA gather
+ * kernel writes pinned host blocks straight into GPU-resident pages).  Pairs
+ * with a slot or block out of range (the -1 padding) are skipped.
+ *   K_host, V_host  HOST pointers to pinned, device-mapped memory, bf16
+ *                   [rows][nb * block_tokens][d], 16-byte aligned
+ *   K_pool, V_pool  bf16 [rows][S * block_tokens][d], 16-byte aligned
+ * Errors: SDQ_EINVAL on null pointers, rows, nb, S or block_tokens < 1,
+ * cap < 0, d != 128, more than 2^24 tokens per row, misalignment, host
+ * memory the device cannot address. */
+int oasis_fetch(const uint16_t* K_host, const uint16_t* V_host, const int32_t* plan_slot,
+                const int32_t* plan_block, int rows, int cap, int nb, int block_tokens, int d,
+                uint16_t* K_pool, uint16_t* V_pool, int S, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -45,6 +45,10 @@ _SIGS = {
     "gather_attend_workspace_bytes": ([_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int], _c_size),
     "gather_attend": ([_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                        _c_int, _f, _vp, _vp, _c_size, _vp], _c_int),
+    "oasis_select": ([_vp, _c_int, _vp, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp,
+                      _vp, _vp], _c_int),
+    "oasis_fetch": ([_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _c_int, _vp],
+                    _c_int),
     "gather_attend_host_kv": ([_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                _c_int, _c_int, _f, _vp, _vp, _c_size, _vp], _c_int),
 }
@@ -424,3 +428,79 @@ def gather_attend(q, K, V, idx, block_tokens=1, per_query_head=False, softmax_sc
                                 int(block_tokens), d, scale, _vp(out.data_ptr()), _vp(ws.data_ptr()),
                                 ws.numel(), _stream(stream)), "gather_attend")
     return out
+
+
+# ------------------------------------------------------------------ resident pool
+class BlockPool:
+    """A GPU-resident block pool per row (request x KV head): the block id held
+    by each of S slots (-1 = empty) and the step at which it was last
+    selected."""
+
+    def __init__(self, rows, S, device="cuda"):
+        self.resident = torch.full((rows, S), -1, dtype=torch.int32, device=device)
+        self.last_sel = torch.zeros((rows, S), dtype=torch.int32, device=device)
+
+
+def oasis_select(pred, block_scores, pool, step, cap, plan_slot=None, plan_block=None,
+                 n_fetch=None, slots=None, stream=None):
+    """pred int32 [rows][K] (predicted block ids), block_scores float32
+    [rows][nb]; pool (BlockPool) updated in place -> (plan_slot, plan_block
+    int32 [rows][cap], n_fetch int32 [rows], slots int32 [rows][S])."""
+    rows, K = pred.shape
+    nb = block_scores.shape[1]
+    S = pool.resident.shape[1]
+    _dev(pred, "pred", 4, rows * K)
+    _dev(block_scores, "block_scores", 4, rows * nb)
+    _dev(pool.resident, "resident", 4, rows * S)
+    _dev(pool.last_sel, "last_sel", 4, rows * S)
+    dv = pred.device
+    plan_slot = _out(plan_slot, (rows, cap), torch.int32, dv, "plan_slot", 4)
+    plan_block = _out(plan_block, (rows, cap), torch.int32, dv, "plan_block", 4)
+    n_fetch = _out(n_fetch, (rows,), torch.int32, dv, "n_fetch", 4)
+    slots = _out(slots, (rows, S), torch.int32, dv, "slots", 4)
+    _check(load().oasis_select(_vp(pred.data_ptr()), K, _vp(block_scores.data_ptr()), nb, rows,
+                               _vp(pool.resident.data_ptr()), _vp(pool.last_sel.data_ptr()), S,
+                               int(step), int(cap), _vp(plan_slot.data_ptr()), _vp(plan_block.data_ptr()),
+                               _vp(n_fetch.data_ptr()), _vp(slots.data_ptr()), _stream(stream)),
+           "oasis_select")
+    return plan_slot, plan_block, n_fetch, slots
+
+
+def oasis_fetch(K_host, V_host, plan_slot, plan_block, K_pool, V_pool, block_tokens=16, stream=None):
+    """K_host, V_host pinned bf16 [rows][nb*bt][128]; K_pool, V_pool device bf16
+    [rows][S*bt][128]: copies the planned blocks into their slots."""
+    if K_host.dim() != 3:
+        raise SDQError("K_host must be [rows][nb*block_tokens][128]")
+    rows, n_host, _ = K_host.shape
+    for t, nm in ((K_host, "K_host"), (V_host, "V_host")):
+        if t.is_cuda or not t.is_pinned() or not t.is_contiguous() or t.element_size() != 2:
+            raise SDQError(f"{nm} must be a contiguous pinned host tensor of 2-byte elements")
+        if t.shape != (rows, n_host, D):
+            raise SDQError(f"{nm} must be [rows][nb*block_tokens][128]")
+    if n_host % block_tokens:
+        raise SDQError("host rows must hold whole blocks")
+    nb = n_host // block_tokens
+    S = K_pool.shape[1] // block_tokens
+    cap = plan_slot.shape[1]
+    _dev(K_pool, "K_pool", 2, rows * S * block_tokens * D)
+    _dev(V_pool, "V_pool", 2, rows * S * block_tokens * D)
+    _dev(plan_slot, "plan_slot", 4, rows * cap)
+    _dev(plan_block, "plan_block", 4, rows * cap)
+    _check(load().oasis_fetch(_vp(K_host.data_ptr()), _vp(V_host.data_ptr()), _vp(plan_slot.data_ptr()),
+                              _vp(plan_block.data_ptr()), rows, cap, nb, int(block_tokens), D,
+                              _vp(K_pool.data_ptr()), _vp(V_pool.data_ptr()), S, _stream(stream)),
+           "oasis_fetch")
+
+
+def attend_stacked(q, q_draft, K_pool, V_pool, slots, block_tokens=16, ws=None, stream=None):
+    """The normal and the draft query rows of each KV head attend over the same
+    resident blocks in one gather_attend call (each set is read once for both).
+    q, q_draft float32 [R][Hq][128]; K_pool, V_pool bf16 [R][Hkv][S*bt][128];
+    slots int32 [R][Hkv][S] -> (out, out_draft) float32 [R][Hq][128]."""
+    R, Hq, d = q.shape
+    Hkv = K_pool.shape[1]
+    grp = Hq // Hkv
+    qs = torch.cat([q.view(R, Hkv, grp, d), q_draft.view(R, Hkv, grp, d)], dim=2).reshape(R, 2 * Hq, d)
+    out = gather_attend(qs.contiguous(), K_pool, V_pool, slots, block_tokens=block_tokens, ws=ws,
+                        stream=stream).view(R, Hkv, 2 * grp, d)
+    return out[:, :, :grp].reshape(R, Hq, d), out[:, :, grp:].reshape(R, Hq, d)

@@ -75,6 +75,15 @@ def test_invalid_arguments_rejected_without_launch():
     assert L.gather_attend(p, p, p, p, 1, 32, 8, 0, 1 << 23, 1 << 23, 512, 1, 128, 1.0, p, p, 1 << 20,
                            s) == EINVAL
     assert L.gather_attend(p, p, p, p, 1, 32, 8, 0, 2001, 2000, 8, 1, 128, 1.0, p, p, 1 << 20, s) == EINVAL
+    assert L.oasis_select(p, 1025, p, 64, 4, p, p, 16, 0, 2, p, p, p, null, s) == EINVAL    # K
+    assert L.oasis_select(p, 16, p, 64, 4, p, p, 0, 0, 2, p, p, p, null, s) == EINVAL       # S
+    assert L.oasis_select(p, 16, p, 70000, 4, p, p, 16, 0, 2, p, p, p, null, s) == EINVAL   # nb
+    assert L.oasis_select(p, 16, p, 64, 4, p, p, 16, 0, -1, p, p, p, null, s) == EINVAL     # cap
+    assert L.oasis_select(p, 16, p, 64, 0, p, p, 16, 0, 2, p, p, p, null, s) == EINVAL      # rows
+    assert L.oasis_select(p, 16, p, 64, 4, null, p, 16, 0, 2, p, p, p, null, s) == EINVAL
+    assert L.oasis_fetch(p, p, p, p, 4, 2, 8, 16, 64, p, p, 8, s) == EINVAL                 # d
+    assert L.oasis_fetch(p, p, p, p, 0, 2, 8, 16, 128, p, p, 8, s) == EINVAL                # rows
+    assert L.oasis_fetch(p, p, p, p, 4, 2, 8, 16, 128, ctypes.c_void_p(0x1008), p, 8, s) == EINVAL  # align
 
 
 def test_workspace_sizes():
