@@ -11,76 +11,87 @@
 
 namespace sdq {
 
-// One workgroup of 256 threads per (KV head, 64-token block).  The block's
-// 64 key rows (16 KB) come in as coalesced 16-byte loads and are staged in
-// LDS; thread (j, h) then takes channel j: the min and max over the block's
-// 64 rows, then the codes of tokens 32h..32h+31, i.e. one word of each of the
-// four planes.  A workgroup covers blocks [b0, b0 + nblk) of one head along
-// gridDim.x.
+// One workgroup of 1024 threads per (KV head, 64-token block).  The block's
+// 64 key rows (16 KB) come in as one coalesced 16-byte load per thread and are
+// staged in LDS.  Thread (j, q) takes channel j and the eight tokens
+// 8q..8q+7: their min and max go to LDS, every thread then reduces the eight
+// partials of its channel, codes its eight tokens (one IEEE division each)
+// and ORs their bits into the block's plane words in LDS; 128 threads write
+// the 2 words x 4 planes of each channel and its metadata.  A workgroup
+// covers blocks [b0, b0 + nblk) of one head along gridDim.x.
 //
 // Rows are n_cap tokens long (the cache's capacity) and the first n tokens
 // are present.  A partly filled last block (the open block of a growing
 // cache) is quantised over its m present tokens: rows past them are staged as
 // copies of the last present row, which leaves the block's min and max
 // unchanged, and the absent tokens' plane bits are cleared.
-constexpr int kApThreads = 256;
+constexpr int kApThreads = 1024;
 
 __global__ __launch_bounds__(kApThreads) void fathom_append_kernel(
     const uint4* __restrict__ keys, int n_cap, int n, int b0, uint32_t* __restrict__ planes,
     uint32_t* __restrict__ meta) {
   __shared__ uint16_t s_k[64][kHeadDim];
+  __shared__ float s_mn[8][kHeadDim], s_mx[8][kHeadDim];
+  __shared__ uint32_t s_w[kHeadDim][8];                   // [channel][plane * 2 + half]
   const int g = blockIdx.y;
   const int b = b0 + blockIdx.x;
   const int t = threadIdx.x;
   const int m = n - b * 64 < 64 ? n - b * 64 : 64;          // present tokens, >= 1
   const uint4* src = keys + (size_t(g) * n_cap + size_t(b) * 64) * (kHeadDim / 8);
-  uint4 v[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {                              // 1024 16-byte pieces, 4 per thread
-    const int f = e * kApThreads + t;
-    const int row = f >> 4;
-    v[e] = src[size_t(row < m ? row : m - 1) * (kHeadDim / 8) + (f & 15)];
+  {
+    const int row = t >> 4;                                  // 16 pieces of 16 bytes per row
+    const uint4 v = src[size_t(row < m ? row : m - 1) * (kHeadDim / 8) + (t & 15)];
+    reinterpret_cast<uint4*>(&s_k[row][0])[t & 15] = v;
   }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int f = e * kApThreads + t;
-    reinterpret_cast<uint4*>(&s_k[f >> 4][0])[f & 15] = v[e];
-  }
-  __syncthreads();
-
   const int j = t & (kHeadDim - 1);
-  const int h = t >> 7;                                      // which 32-token half
+  const int qd = t >> 7;                                     // tokens 8qd..8qd+7
+  (&s_w[0][0])[t] = 0u;                                      // 1024 words, one per thread
+  __syncthreads();
+  float x[8];
   float mn = INFINITY, mx = -INFINITY;
-#pragma unroll 16
-  for (int i = 0; i < 64; ++i) {
-    const float x = __uint_as_float(uint32_t(s_k[i][j]) << 16);
-    mn = fminf(mn, x);
-    mx = fmaxf(mx, x);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    x[i] = __uint_as_float(uint32_t(s_k[8 * qd + i][j]) << 16);
+    mn = fminf(mn, x[i]);
+    mx = fmaxf(mx, x[i]);
+  }
+  s_mn[qd][j] = mn;
+  s_mx[qd][j] = mx;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    mn = fminf(mn, s_mn[u][j]);
+    mx = fmaxf(mx, s_mx[u][j]);
   }
   const _Float16 off16 = _Float16(mn);
   const _Float16 sc16 = _Float16(__fdiv_rn(mx - mn, 15.0f));
   const float off = float(off16);
   const float sc = float(sc16);
-  uint32_t pl[4] = {0, 0, 0, 0};
-#pragma unroll 8
-  for (int i = 0; i < 32; ++i) {
-    const float x = __uint_as_float(uint32_t(s_k[32 * h + i][j]) << 16);
-    float r = (sc == 0.0f) ? 0.0f : rintf(__fdiv_rn(x - off, sc));
+  uint32_t bits[4] = {0, 0, 0, 0};                           // this thread's 8 tokens, per plane
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float r = (sc == 0.0f) ? 0.0f : rintf(__fdiv_rn(x[i] - off, sc));
     r = fminf(fmaxf(r, 0.0f), 15.0f);
-    const uint32_t code = uint32_t(r);
+    const uint32_t code = 8 * qd + i < m ? uint32_t(r) : 0u; // absent tokens hold code 0
 #pragma unroll
-    for (int p = 0; p < 4; ++p) pl[p] |= ((code >> (3 - p)) & 1u) << i;
+    for (int p = 0; p < 4; ++p) bits[p] |= ((code >> (3 - p)) & 1u) << i;
   }
-  const int mh = m - 32 * h;                                 // present tokens of this half
-  const uint32_t keep = mh >= 32 ? 0xFFFFFFFFu : (mh > 0 ? (1u << mh) - 1u : 0u);
-  const size_t nw = size_t(n_cap) / 32;                      // 32-token words per plane row
-  uint32_t* prow = planes + (size_t(g) * kHeadDim + j) * 4 * nw + 2 * size_t(b) + h;
+  const int half = qd >> 2, sh = 8 * (qd & 3);               // position inside the 32-token word
 #pragma unroll
-  for (int p = 0; p < 4; ++p) prow[size_t(p) * nw] = pl[p] & keep;
-  if (h == 0)
-    meta[(size_t(g) * kHeadDim + j) * (n_cap / 64) + b] =
+  for (int p = 0; p < 4; ++p) atomicOr(&s_w[j][p * 2 + half], bits[p] << sh);
+  __syncthreads();
+  if (t < kHeadDim) {
+    const size_t nw = size_t(n_cap) / 32;                    // 32-token words per plane row
+    uint32_t* prow = planes + (size_t(g) * kHeadDim + t) * 4 * nw + 2 * size_t(b);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      prow[size_t(p) * nw] = s_w[t][p * 2];
+      prow[size_t(p) * nw + 1] = s_w[t][p * 2 + 1];
+    }
+    meta[(size_t(g) * kHeadDim + t) * (n_cap / 64) + b] =
         uint32_t(__builtin_bit_cast(uint16_t, sc16)) |
         (uint32_t(__builtin_bit_cast(uint16_t, off16)) << 16);
+  }
 }
 
 __device__ __forceinline__ uint32_t f16_next_down(uint32_t h) {
