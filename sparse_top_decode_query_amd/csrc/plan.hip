@@ -10,9 +10,10 @@ __global__ __launch_bounds__(64) void fathom_plan_kernel(const float* __restrict
                                                          const float* __restrict__ var, int Hgrp,
                                                          int budget, uint8_t* __restrict__ depth,
                                                          float* __restrict__ qbar) {
+  __shared__ uint32_t s_scratch[kHeadDim];
   const int g = blockIdx.x;
   const int l = threadIdx.x;
-  const HeadPlan p = plan_head<UNIFORM>(q, var, g, Hgrp, budget);
+  const HeadPlan p = plan_head<UNIFORM>(q, var, g, Hgrp, budget, s_scratch);
   qbar[size_t(g) * kHeadDim + l] = p.a0;
   qbar[size_t(g) * kHeadDim + l + 64] = p.a1;
   depth[size_t(g) * kHeadDim + l] = uint8_t(p.d0);

@@ -12,6 +12,14 @@
 // the bits with gain == T the first B - #(gain > T) in (j, t) order.  The
 // uniform baseline plan takes the n_channels channels of largest w_j (ties to
 // the lower channel), each at depth 4.
+//
+// The search first fixes T's exponent field (8 steps).  When that exponent is
+// not 0, the candidates sharing it hold at most one bit per channel (a
+// channel's normal gains are 2 binades apart), so at most 128 of them exist:
+// they are compacted into `lds` (128 words, private to the wave) and T is the
+// one whose rank among them is the one still needed, found by counting
+// instead of 23 more dependent search steps.  A zero exponent (subnormal
+// gains, or infinite ones) continues the bitwise search instead.
 #pragma once
 #include "common.hpp"
 
@@ -28,7 +36,7 @@ struct HeadPlan {
 template <bool UNIFORM>
 __device__ __forceinline__ HeadPlan plan_head(const float* __restrict__ q,
                                               const float* __restrict__ var, int g, int Hgrp,
-                                              int budget) {
+                                              int budget, uint32_t* lds) {
   const int l = threadIdx.x & 63;
   const int j0 = l, j1 = l + 64;
   const float* qg = q + size_t(g) * Hgrp * kHeadDim;
@@ -68,14 +76,55 @@ __device__ __forceinline__ HeadPlan plan_head(const float* __restrict__ q,
   const int total = NT * kHeadDim;
   const int K = budget < total ? budget : total;
 
+  const uint64_t lt = (l == 0) ? 0ull : (~0ull >> (64 - l));
   uint32_t T = 0;
-  if (K > 0) {
-    for (int bit = 30; bit >= 0; --bit) {
+  auto search = [&](int hi, int lo) {
+    for (int bit = hi; bit >= lo; --bit) {
       const uint32_t cand = T | (1u << bit);
       int cnt = 0;
 #pragma unroll
       for (int t = 0; t < NT; ++t) cnt += wave_count(v0[t] >= cand) + wave_count(v1[t] >= cand);
       if (cnt >= K) T = cand;
+    }
+  };
+  if (K > 0) {
+    search(30, 23);                                  // exponent field of T
+    const uint32_t e = T >> 23;
+    if (e == 0 || e == 255) {                       // subnormal or infinite gains
+      search(22, 0);
+    } else {
+      // the bucket: candidates with T's exponent; r = rank of T within it
+      const uint32_t above_cut = (e + 1) << 23;
+      int above = 0;
+      uint32_t u0 = 0, u1 = 0;
+      bool h0 = false, h1 = false;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        above += wave_count(v0[t] >= above_cut) + wave_count(v1[t] >= above_cut);
+        if ((v0[t] >> 23) == e) { u0 = v0[t]; h0 = true; }
+        if ((v1[t] >> 23) == e) { u1 = v1[t]; h1 = true; }
+      }
+      const int r = K - above;
+      const uint64_t b0 = __ballot(h0), b1 = __ballot(h1);
+      const int m0 = __popcll(b0), m = m0 + __popcll(b1);
+      if (h0) lds[__popcll(b0 & lt)] = u0;
+      if (h1) lds[m0 + __popcll(b1 & lt)] = u1;
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      int gt0 = 0, ge0 = 0, gt1 = 0, ge1 = 0;
+      for (int i = 0; i < m; ++i) {
+        const uint32_t x = lds[i];
+        gt0 += x > u0;
+        ge0 += x >= u0;
+        gt1 += x > u1;
+        ge1 += x >= u1;
+      }
+      const uint64_t c0 = __ballot(h0 && gt0 < r && r <= ge0);
+      const uint64_t c1 = __ballot(h1 && gt1 < r && r <= ge1);
+      T = c0 ? uint32_t(__builtin_amdgcn_readlane(int(u0), int(__builtin_ctzll(c0))))
+             : uint32_t(__builtin_amdgcn_readlane(int(u1), int(__builtin_ctzll(c1))));
+      __builtin_amdgcn_wave_barrier();              // lds is free again
     }
   }
   int gt = 0;
@@ -83,7 +132,6 @@ __device__ __forceinline__ HeadPlan plan_head(const float* __restrict__ q,
   for (int t = 0; t < NT; ++t) gt += wave_count(v0[t] > T) + wave_count(v1[t] > T);
   const int rem = K - gt;                  // bits to take among those equal to T
 
-  const uint64_t lt = (l == 0) ? 0ull : (~0ull >> (64 - l));
   int before0 = 0, total0 = 0, before1 = 0;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
