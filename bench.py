@@ -58,9 +58,10 @@ def parse_args():
                     help="skip the plan variants, the host-resident index and configs 4/5")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain 512 MiB device copies (for counter calibration)")
-    ap.add_argument("--variant", choices=("hamming", "minmax"),
-                    help="run only the config 4 (hamming) or config 5 (minmax) step, for "
-                         "kernel traces; prints one JSON line about that step")
+    ap.add_argument("--variant", choices=("hamming", "minmax", "oasis"),
+                    help="run only the config 4 (hamming) step, the config 5 (minmax) step or the "
+                         "resident-pool step on the config 5 layer, for kernel traces; prints one "
+                         "JSON line about that step")
     return ap.parse_args()
 
 
@@ -476,6 +477,9 @@ def variant_oasis(torch, np, lib, synth, dev, steps=10, cap=16, drift=0.25):
     g = np.random.default_rng(synth.seed_of(5) + 1)
     drafts = [q + drift * torch.from_numpy(g.standard_normal(mm["q"].shape, dtype=np.float32)).to(dev)
               for _ in range(steps + 1)]
+    # the projection hands attention the normal and draft rows already stacked
+    stacked = [lib.stacked_layout(q, dq, Gm) for dq in drafts]
+    out_s = torch.empty(R, 2 * Gm * Hg, 128, device=dev)
     pool = lib.BlockPool(rows, S, dev)
     Kp = torch.zeros(rows, S * 16, 128, dtype=torch.int16, device=dev)
     Vp = torch.zeros_like(Kp)
@@ -505,8 +509,8 @@ def variant_oasis(torch, np, lib, synth, dev, steps=10, cap=16, drift=0.25):
         ev[3].record()
         lib.oasis_fetch(Kh, Vh, ps, pb, Kp, Vp, 16)
         ev[4].record()
-        lib.attend_stacked(q, drafts[t], Kp.view(R, Gm, S * 16, 128), Vp.view(R, Gm, S * 16, 128),
-                           slots.view(R, Gm, S), 16, ws=ws_a)
+        lib.attend_stacked(stacked[t], Kp.view(R, Gm, S * 16, 128), Vp.view(R, Gm, S * 16, 128),
+                           slots.view(R, Gm, S), 16, out=out_s, ws=ws_a)
         ev[5].record()
         torch.cuda.synchronize()
         for i, k_ in enumerate(names):
@@ -606,8 +610,9 @@ def variant_minmax(torch, np, lib, bytemodel, synth, dev, timeit):
 
 
 def run_variant(args):
-    """--variant hamming|minmax: only that step, W warm-up + K steps, for kernel
-    traces of the variant kernels; prints one JSON line about it."""
+    """--variant hamming|minmax|oasis: only that step, W warm-up + K steps (the
+    resident-pool step fills its pool first, untimed, and times K steps), for
+    kernel traces of the variant kernels; prints one JSON line about it."""
     import numpy as np
     import torch
     import synth
@@ -616,6 +621,10 @@ def run_variant(args):
         raise SystemExit("bench.py needs a GPU")
     lib.load()
     dev = torch.device("cuda:0")
+    if args.variant == "oasis":
+        info = variant_oasis(torch, np, lib, synth, dev, steps=args.steps)
+        print(json.dumps({"variant": "oasis", **info}), flush=True)
+        return
     setup = setup_hamming if args.variant == "hamming" else setup_minmax
     step, _, _ = setup(torch, np, lib, synth, dev)
     for i in range(args.warmup):

@@ -492,15 +492,28 @@ def oasis_fetch(K_host, V_host, plan_slot, plan_block, K_pool, V_pool, block_tok
            "oasis_fetch")
 
 
-def attend_stacked(q, q_draft, K_pool, V_pool, slots, block_tokens=16, ws=None, stream=None):
-    """The normal and the draft query rows of each KV head attend over the same
-    resident blocks in one gather_attend call (each set is read once for both).
-    q, q_draft float32 [R][Hq][128]; K_pool, V_pool bf16 [R][Hkv][S*bt][128];
-    slots int32 [R][Hkv][S] -> (out, out_draft) float32 [R][Hq][128]."""
+def attend_stacked(q_stacked, K_pool, V_pool, slots, block_tokens=16, out=None, ws=None,
+                   stream=None):
+    """The normal and draft queries of each KV head attend over the same
+    resident blocks in one gather_attend call, so each block is read once for
+    both.  q_stacked float32 [R][Hkv*2*grp][128], per KV head its grp normal
+    query rows followed by its grp draft rows; K_pool, V_pool bf16
+    [R][Hkv][S*bt][128]; slots int32 [R][Hkv][S] -> out float32 in q_stacked's
+    layout (unstack_outputs splits it)."""
+    return gather_attend(q_stacked, K_pool, V_pool, slots, block_tokens=block_tokens, out=out,
+                         ws=ws, stream=stream)
+
+
+def stacked_layout(q, q_draft, Hkv):
+    """q, q_draft [R][Hq][128] -> q_stacked [R][2*Hq][128] for attend_stacked."""
     R, Hq, d = q.shape
-    Hkv = K_pool.shape[1]
     grp = Hq // Hkv
-    qs = torch.cat([q.view(R, Hkv, grp, d), q_draft.view(R, Hkv, grp, d)], dim=2).reshape(R, 2 * Hq, d)
-    out = gather_attend(qs.contiguous(), K_pool, V_pool, slots, block_tokens=block_tokens, ws=ws,
-                        stream=stream).view(R, Hkv, 2 * grp, d)
-    return out[:, :, :grp].reshape(R, Hq, d), out[:, :, grp:].reshape(R, Hq, d)
+    return torch.cat([q.view(R, Hkv, grp, d), q_draft.view(R, Hkv, grp, d)], dim=2).reshape(R, 2 * Hq, d)
+
+
+def unstack_outputs(out, Hkv):
+    """attend_stacked's output -> (out, out_draft) [R][Hq][128]."""
+    R, H2, d = out.shape
+    grp = H2 // (2 * Hkv)
+    o = out.view(R, Hkv, 2 * grp, d)
+    return o[:, :, :grp].reshape(R, Hkv * grp, d), o[:, :, grp:].reshape(R, Hkv * grp, d)

@@ -139,9 +139,10 @@ def test_oasis_selection_step_end_to_end(sdq):
         pred = sdq.topk_select(scores, k, n_local=1)
         ps, pb, nf, slots = sdq.oasis_select(pred, scores, pool, step, cap)
         sdq.oasis_fetch(Kh, Vh, ps, pb, Kp, Vp, bt)
-        out, out_d = sdq.attend_stacked(torch.from_numpy(q).cuda(), torch.from_numpy(q_draft).cuda(),
-                                        Kp.view(R, G, S * bt, 128), Vp.view(R, G, S * bt, 128),
-                                        slots.view(R, G, S), bt)
+        qs = sdq.stacked_layout(torch.from_numpy(q).cuda(), torch.from_numpy(q_draft).cuda(), G)
+        out_s = sdq.attend_stacked(qs, Kp.view(R, G, S * bt, 128), Vp.view(R, G, S * bt, 128),
+                                   slots.view(R, G, S), bt)
+        out, out_d = sdq.unstack_outputs(out_s, G)
         torch.cuda.synchronize()
         # selection parity on the GPU's own scores and top-K
         S_g, P_g = host(scores), host(pred)
