@@ -10,7 +10,7 @@ __global__ __launch_bounds__(64) void fathom_plan_kernel(const float* __restrict
                                                          const float* __restrict__ var, int Hgrp,
                                                          int budget, uint8_t* __restrict__ depth,
                                                          float* __restrict__ qbar) {
-  __shared__ uint32_t s_scratch[kHeadDim];
+  __shared__ __attribute__((aligned(16))) uint32_t s_scratch[3 * kHeadDim];
   const int g = blockIdx.x;
   const int l = threadIdx.x;
   const HeadPlan p = plan_head<UNIFORM>(q, var, g, Hgrp, budget, s_scratch);

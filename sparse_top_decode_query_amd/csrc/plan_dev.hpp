@@ -13,13 +13,15 @@
 // uniform baseline plan takes the n_channels channels of largest w_j (ties to
 // the lower channel), each at depth 4.
 //
-// The search first fixes T's exponent field (8 steps).  When that exponent is
-// not 0, the candidates sharing it hold at most one bit per channel (a
-// channel's normal gains are 2 binades apart), so at most 128 of them exist:
-// they are compacted into `lds` (128 words, private to the wave) and T is the
-// one whose rank among them is the one still needed, found by counting
-// instead of 23 more dependent search steps.  A zero exponent (subnormal
-// gains, or infinite ones) continues the bitwise search instead.
+// T's exponent field comes from a 256-bin histogram of the candidates'
+// exponent fields in LDS and one wave scan over it (the largest exponent e
+// with at least K candidates at or above it).  When that exponent is not 0,
+// the candidates sharing it hold at most one bit per channel (a channel's
+// normal gains are 2 binades apart), so at most 128 of them exist: they are
+// compacted into LDS and T is the one whose rank among them is the one still
+// needed, found by counting instead of 23 dependent search steps.  A zero
+// exponent (subnormal gains, or infinite ones) takes the bitwise search over
+// the mantissa instead.  `lds` is 384 words private to the wave.
 #pragma once
 #include "common.hpp"
 
@@ -87,20 +89,45 @@ __device__ __forceinline__ HeadPlan plan_head(const float* __restrict__ q,
       if (cnt >= K) T = cand;
     }
   };
+  auto lds_sync = [] {
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
   if (K > 0) {
-    search(30, 23);                                  // exponent field of T
-    const uint32_t e = T >> 23;
+    // exponent field of T from a histogram of the candidates' exponent fields
+    uint32_t* hist = lds + kHeadDim;                 // 256 bins after the bucket
+    reinterpret_cast<uint4*>(hist)[l] = make_uint4(0u, 0u, 0u, 0u);
+    lds_sync();
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      atomicAdd(&hist[v0[t] >> 23], 1u);
+      atomicAdd(&hist[v1[t] >> 23], 1u);
+    }
+    lds_sync();
+    const uint4 c4 = reinterpret_cast<const uint4*>(hist)[l];     // bins 4l .. 4l+3
+    const int s4 = int(c4.x + c4.y + c4.z + c4.w);
+    const int inc = wave_incl_scan(s4);
+    const int ge3 = wave_last(inc) - inc + int(c4.w);             // candidates with exponent >= 4l+3
+    const int ge2 = ge3 + int(c4.z), ge1 = ge2 + int(c4.y), ge0 = ge1 + int(c4.x);
+    // the largest e with ge(e) >= K: ge falls as e rises, so the lanes with
+    // such a bin are a prefix of the wave and e is the top one of the last
+    const int eb = ge3 >= K ? 3 : (ge2 >= K ? 2 : (ge1 >= K ? 1 : (ge0 >= K ? 0 : -1)));
+    const int abv = eb == 3 ? ge3 - int(c4.w) : (eb == 2 ? ge3 : (eb == 1 ? ge2 : ge1));
+    const uint64_t own = __ballot(eb >= 0);
+    const int src_lane = 63 - __builtin_clzll(own);
+    const uint32_t e = uint32_t(__builtin_amdgcn_readlane(4 * l + eb, src_lane));
+    const int above = __builtin_amdgcn_readlane(abv, src_lane);  // candidates with exponent > e
+    T = e << 23;
+    lds_sync();
     if (e == 0 || e == 255) {                       // subnormal or infinite gains
       search(22, 0);
     } else {
       // the bucket: candidates with T's exponent; r = rank of T within it
-      const uint32_t above_cut = (e + 1) << 23;
-      int above = 0;
       uint32_t u0 = 0, u1 = 0;
       bool h0 = false, h1 = false;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        above += wave_count(v0[t] >= above_cut) + wave_count(v1[t] >= above_cut);
         if ((v0[t] >> 23) == e) { u0 = v0[t]; h0 = true; }
         if ((v1[t] >> 23) == e) { u1 = v1[t]; h1 = true; }
       }

@@ -191,6 +191,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
       s_qbar[lane + 64] = qbar[size_t(g) * kHeadDim + lane + 64];
     } else {
       // s_out is not used before the scores, so it lends the plan its scratch
+      // (384 words)
       const HeadPlan p = plan_head<MODE == 2>(pin.q, pin.var, g, pin.Hgrp, pin.budget,
                                               reinterpret_cast<uint32_t*>(&s_out[0][0]));
       t0 = p.d0;

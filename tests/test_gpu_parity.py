@@ -127,6 +127,31 @@ def test_fathom_plan_ties_and_uniform(sdq):
         assert np.array_equal(host(depth), rd), nch
 
 
+def test_fathom_plan_gain_extremes(sdq):
+    """Gains in the subnormal range, mixed with normal ones, and exact powers of
+    four that tie across channels and depths, against the oracle bit for bit."""
+    _say("plan gain extremes")
+    g = np.random.default_rng(5)
+    G, Hgrp = 5, 2
+    q = g.standard_normal((G * Hgrp, 128)).astype(np.float32)
+    var = np.ones((G, 128), np.float32)
+    q[0:2] *= np.float32(1e-5)
+    var[0] = np.float32(1e-30)                                   # every gain subnormal
+    var[1, :64] = np.float32(1e-30)                              # half subnormal, half normal
+    q[4:6] = np.float32(0.5)                                     # qbar = 1 on head 2
+    var[2] = (4.0 ** g.integers(-6, 6, 128)).astype(np.float32)  # gains are powers of four
+    var[3] = np.exp(g.uniform(-40, 40, 128)).astype(np.float32)  # a wide exponent range
+    q[8:10, :100] = 0.0                                          # head 4: few nonzero gains
+    for budget in (1, 7, 56, 200, 511, 512):
+        depth, qbar = sdq.fathom_plan(dev(q), dev(var), budget)
+        rd, rq = o_fathom.plan_heads(q, var, Hgrp, budget=budget)
+        assert np.array_equal(host(depth), rd), budget
+    for nch in (1, 34, 100):
+        depth, _ = sdq.fathom_plan(dev(q), dev(var), 0, uniform_channels=nch)
+        rd, _ = o_fathom.plan_heads(q, var, Hgrp, n_uniform=nch)
+        assert np.array_equal(host(depth), rd), nch
+
+
 # ---------------------------------------------------------------- scan
 def _scan_case(sdq, G, n, budget, uniform=None):
     case = synth.fathom_case(2, n=n, heads=list(range(G)), with_values=False)
