@@ -361,7 +361,9 @@ def _rand_kv(g, R, Hkv, n):
                                                     (2, 8, 4, 700, 333, False, 1),      # 2 heads per set
                                                     (1, 32, 4, 2048, 1000, False, 1),   # 8 heads per set
                                                     (1, 8, 2, 999, 40, False, 3),       # 3-row blocks
-                                                    (1, 8, 2, 3000, 2900, False, 1)])   # 23 splits, ragged
+                                                    (1, 8, 2, 3000, 2900, False, 1),    # 23 splits, ragged
+                                                    (1, 32, 4, 2048, 400, False, 1),    # 8 heads, 8-wave sets
+                                                    (1, 16, 4, 1024, 300, True, 1)])    # per head, 8-wave sets
 def test_gather_attend_parity(sdq, R, Hq, Hkv, n, m, per_qh, bt):
     _say(f"attend R={R} Hq={Hq} Hkv={Hkv} n={n} m={m} per_qh={per_qh} bt={bt}")
     g = np.random.default_rng(n + m)
