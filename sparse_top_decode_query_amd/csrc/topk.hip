@@ -820,8 +820,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __rest
   __shared__ uint32_t sbin[kBmBins];
   __shared__ int cb[kBmCandBlocks];       // candidate block numbers, ascending
   __shared__ int s_cnt[640];              // kept keys per block of a chunk, then offsets
-  __shared__ float ckey[kBmCap + 64];     // + a discard slot per lane
-  __shared__ int cidx[kBmCap + 64];
+  __shared__ float ckey[kBmCap];
+  __shared__ int cidx[kBmCap];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t s_red[2 * kTkWaves];
   __shared__ int s_scan[2 * kTkWaves];
@@ -991,9 +991,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __rest
         firsts[r] = (blo + cb[cc + (c < nch ? c : 0)]) * 64 + 4 * q;
       }
       // candidates are sparse (about one per block): a round is skipped
-      // unless some lane of the wave holds one, and inside a round every lane
-      // writes its 4 keys, those below thr to its own discard slot, so no
-      // lane-divergent branch is needed
+      // unless some lane of the wave holds one, and inside a round only the
+      // kept keys are written (under the lane mask)
 #pragma unroll
       for (int r = 0; r < kRC; ++r) {
         const int c = r * 32 + grp;
@@ -1006,9 +1005,10 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __rest
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const bool keep = c < nch && xs[e] >= thr;
-          const int p = keep ? pos : kBmCap + lane;
-          ckey[p] = xs[e];
-          cidx[p] = first + e;
+          if (keep) {
+            ckey[pos] = xs[e];
+            cidx[pos] = first + e;
+          }
           pos += keep;
         }
       }
