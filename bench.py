@@ -21,9 +21,11 @@ write) over its average launch time, measured with HIP events on the stream
 the kernels run on.  `roofline_valu` prices the same launches against the
 vector ALU (one weighted accumulate per plane bit per token).
 `cpu_baseline` is the CPU oracle (fp64 NumPy) timed on the host on the same
-1M-token workload, one KV head at a time.
+1M-token workload, one KV head at a time on one thread;
+`cpu_baseline_all_cores` runs the heads on one thread each.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu] [--no-extras] [--variant hamming|minmax]
+    python bench.py [--steps K] [--warmup W] [--no-cpu] [--no-extras]
+                    [--variant hamming|minmax|oasis]
 """
 from __future__ import annotations
 
