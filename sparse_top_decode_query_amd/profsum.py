@@ -13,6 +13,11 @@
         output also records the SHA-256 of the scan source and of the plan, so
         a consumer can tell when the figures no longer describe the kernel.
 
+    python -m sparse_top_decode_query_amd.profsum counters OUT DB [DB ...] \
+            --kernel fathom_scan --command CMD [--command CMD] [--clocks FILE]
+        per-dispatch means of the SQ counters of one or more `--pmc` runs, and
+        the rocm-smi clock listing of the box if given.
+
 Reads SQLite only; nothing here touches the GPU.
 """
 from __future__ import annotations
@@ -99,6 +104,33 @@ def traffic_summary(fetch_db, write_db, kernel, copy_bytes, plan_sha, cmd_fetch,
     ]) + "\n"
 
 
+def counters_summary(dbs, kernel, commands, clocks_file=None):
+    """Per-dispatch means (summed over a dispatch's counter instances) of every
+    counter in the given `--pmc` result databases, for one kernel."""
+    lines = [f"# rocprofv3 counters of {kernel} per dispatch"]
+    lines += [f"command: {c}" for c in commands]
+    vals = {}
+    for db_path in dbs:
+        db = sqlite3.connect(db_path)
+        names = [r[0] for r in db.execute("select distinct counter_name from counters_collection")]
+        for cn in names:
+            mean, nd = counter_per_dispatch(db_path, cn, kernel)
+            vals[cn] = (mean, nd)
+    lines.append(f"kernel: {kernel}")
+    for cn in sorted(vals):
+        lines.append(f"{cn}: {vals[cn][0]:.6g}  (dispatches {vals[cn][1]})")
+    if "SQ_INSTS_VALU" in vals:
+        lines.append(f"valu_lane_ops (SQ_INSTS_VALU x 64): {vals['SQ_INSTS_VALU'][0] * 64:.6g}")
+    if "SQ_ACTIVE_INST_VALU" in vals and "SQ_BUSY_CYCLES" in vals:
+        lines.append("note: counter meanings as listed by `rocprofv3 --list-avail` on the box")
+    if clocks_file and os.path.exists(clocks_file):
+        lines.append("")
+        lines.append("# rocm-smi --showclocks on the same box")
+        with open(clocks_file) as f:
+            lines += [l.rstrip() for l in f if l.strip() and not set(l.strip()) <= set("=-")]
+    return "\n".join(lines) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -115,9 +147,17 @@ def main(argv=None):
     b.add_argument("--plan-sha256", required=True)
     b.add_argument("--command-fetch", required=True)
     b.add_argument("--command-write", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("out")
+    c.add_argument("dbs", nargs="+")
+    c.add_argument("--kernel", default="fathom_scan")
+    c.add_argument("--command", action="append", required=True)
+    c.add_argument("--clocks", default=None, help="rocm-smi --showclocks output to append")
     args = ap.parse_args(argv)
     if args.cmd == "kernels":
         text = kernels_summary(args.db, args.command)
+    elif args.cmd == "counters":
+        text = counters_summary(args.dbs, args.kernel, args.command, args.clocks)
     else:
         text = traffic_summary(args.fetch_db, args.write_db, args.kernel, args.copy_bytes,
                                args.plan_sha256, args.command_fetch, args.command_write)
