@@ -118,14 +118,21 @@ def cpu_baseline(budget, k, min_seconds=10.0, max_passes=50):
                       case["var"][g:g + 1], case["K"], case["V"]))
     log("cpu oracle: index built for every KV head")
     timed, keys, passes = 0.0, 0, 0
+    stage = {"plan": 0.0, "scan": 0.0, "topk": 0.0, "attend": 0.0}
     while timed < min_seconds and passes < max_passes:
         for n, planes, meta, q, var, K, V in heads:
             t0 = time.perf_counter()
             depth, qbar = o_fathom.plan_heads(q, var, Hgrp, budget=budget)
+            t1 = time.perf_counter()
             s = o_fathom.scan_heads(planes, meta, depth, qbar, n)
+            t2 = time.perf_counter()
             idx = o_select.topk(s[0], k)
+            t3 = time.perf_counter()
             o_attend.attend(q[None], K[None], V[None], idx[None, None])
-            timed += time.perf_counter() - t0
+            t4 = time.perf_counter()
+            for name, dt in zip(stage, (t1 - t0, t2 - t1, t3 - t2, t4 - t3)):
+                stage[name] += dt
+            timed += t4 - t0
             keys += n
         passes += 1
         log(f"cpu oracle: pass {passes}: {timed:.1f} s timed so far")
@@ -137,6 +144,7 @@ def cpu_baseline(budget, k, min_seconds=10.0, max_passes=50):
                    f"B={budget}, k={k}): plan+scan+top-k+attention per head, fp64 NumPy, one thread; "
                    f"index build untimed; host has {os.cpu_count()} logical CPUs"),
         "seconds": round(timed, 2),
+        "stage_ms_per_head": {name: round(v / (passes * G) * 1e3, 2) for name, v in stage.items()},
     }
 
     # the same calls with the KV heads in parallel, one thread each (NumPy
