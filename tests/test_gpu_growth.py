@@ -148,6 +148,27 @@ def test_fathom_scan_ragged_n(sdq, n):
             assert np.array_equal(i_bm[g], ref_i) and np.array_equal(i_gen[g], ref_i)
 
 
+@pytest.mark.parametrize("n", [1, 100, 999])
+def test_uniform_plan_scan_ragged_n(sdq, n):
+    G, Hgrp, n_cap = 2, 4, 1024
+    _say(f"uniform plan + scan ragged n={n}")
+    case = synth.fathom_case(2, n=n_cap, heads=[0, 1], with_values=False)
+    K, q, var = case["K"], case["q"][:G * Hgrp], case["var"][:G]
+    index = _sentinel_index(sdq, G, n_cap)
+    sdq.fathom_append(dev(K), 0, n, index)
+    depth, qbar, scores = sdq.fathom_plan_scan(index, dev(q), dev(var), 0, n, uniform_channels=34)
+    torch.cuda.synchronize()
+    rd, rq = o_fathom.plan_heads(q, var, Hgrp, n_uniform=34)
+    assert np.array_equal(host(depth), rd)
+    rp, rm = o_fathom.ingest(K, n, n_cap)
+    ref = o_fathom.scan_heads(rp, rm, rd, rq, n)
+    S = host(scores)
+    for g in range(G):
+        rng = max(float(ref[g].max() - ref[g].min()), float(np.abs(ref[g]).max()) if n == 1 else 0.0)
+        assert float(np.abs(S[g, :n] - ref[g]).max()) <= SCORE_RTOL * rng + 1e-6
+        assert np.all(np.isneginf(S[g, n:]))
+
+
 def test_decode_loop_on_growing_cache(sdq):
     """Several decode steps on one cache: append the new token, plan + scan the
     first n, top-k over the padded row with the last 64 positions kept as the

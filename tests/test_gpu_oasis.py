@@ -89,6 +89,24 @@ def test_oasis_select_chained_steps_bitexact(sdq, rows, nb, S, K):
         resident, last_sel = _check_step(sdq, pred, scores, resident, last_sel, step, cap)
 
 
+def test_oasis_select_edge_cases(sdq):
+    """A block listed twice in the prediction is one miss; an empty prediction
+    evicts nothing; a cap above the pool size fills every target."""
+    _say("oasis_select edge cases")
+    g = np.random.default_rng(84)
+    nb, S = 50, 6
+    scores = g.standard_normal((2, nb)).astype(np.float32)
+    resident = np.array([[3, -1, 7, 9, -1, 20], [-1, -1, -1, -1, -1, -1]])
+    last_sel = np.array([[1, 0, 2, 0, 0, 5], [0] * 6])
+    pred = np.array([[7, 11, 11, 30, 3, 30], [4, 4, 4, 4, 4, 4]])
+    for cap in (1, 2, 10):
+        # the oracle's prediction is a set, so duplicates collapse there too
+        _check_step(sdq, pred, scores, resident, last_sel, 4, cap)
+    _check_step(sdq, np.zeros((2, 0), np.int64), scores, resident, last_sel, 4, 3)
+    _check_step(sdq, np.array([[0, 1, 2, 4, 5, 6], [8, 9, 10, 11, 12, 13]]), scores, resident,
+                last_sel, 4, 1000)
+
+
 def test_oasis_fetch_matches_plan(sdq):
     _say("oasis_fetch")
     g = np.random.default_rng(82)
