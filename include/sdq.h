@@ -264,6 +264,22 @@ int topk_select_block_max(const float* keys, const float* block_max, int rows, i
 int hamming_scan(const uint32_t* sigs, const uint32_t* qsig, int H, int n, int n_cap,
                  uint8_t* dist, hipStream_t stream);
 
+/* hamming_scan_topk -- hamming_scan followed by topk_select(dist,
+ * SDQ_KEY_U8_MIN, ...) in fewer launches (HashAttention study notes,
+ * sec. 2.1: score every key, then keep the top-k).  On long rows the
+ * distance kernel also writes the per-segment histograms the uint8 selection
+ * reads, so the selection's first pass is not launched; otherwise the two
+ * calls run one after the other.  dist and idx_out are identical to those of
+ * the two separate calls (the selection is deterministic).
+ *   sigs, qsig, H, n, n_cap, dist as hamming_scan (dist is written in full);
+ *   k, n_sink, n_local, idx_out as topk_select with rows = H;
+ *   ws, ws_bytes: at least topk_select_workspace_bytes(H, n, k,
+ *                 SDQ_KEY_U8_MIN) bytes of device memory, owned by the caller
+ * Errors: those of hamming_scan and topk_select. */
+int hamming_scan_topk(const uint32_t* sigs, const uint32_t* qsig, int H, int n, int n_cap, int k,
+                      int n_sink, int n_local, uint8_t* dist, int32_t* idx_out, void* ws,
+                      size_t ws_bytes, hipStream_t stream);
+
 /* minmax_block_scan -- block scores against min/max summaries (OasisKV
  * review, Quest-style summaries):
  *   S[rg][b] = sum over the group's heads h and dims j of

@@ -648,6 +648,89 @@ __global__ __launch_bounds__(kU8SegThreads) void topk_u8_hist_kernel(const uint8
   ws[(size_t(row) * nseg + seg) * 256 + tid] = t;
 }
 
+// Hamming distances and pass 1 in one launch (HashAttention study notes,
+// sec. 2.1 SCORE then TOPK): one workgroup per segment of the competition
+// range computes its tokens' distances popcount(sig XOR qsig), stores them,
+// and writes the segment's 256-bin histogram in the layout
+// topk_u8_hist_kernel writes.  A distance lies in [0, 32], so only 33 bins
+// are counted (in LDS, privatised per wave and lane quarter, odd row stride
+// so that one bin's copies fall in different banks) and the rest are zero.
+// 1024 threads of 16 tokens cover one segment.  One more workgroup per row
+// stores the distances of the sink and local windows [0, lo) and [hi, n).
+// Signature rows are n_cap long.
+constexpr int kHhThreads = 1024;
+constexpr int kHhPer = kU8Seg / kHhThreads;                // 16 tokens per thread
+constexpr int kHhBins = 33;
+constexpr int kHhWaves = kHhThreads / 64;
+
+__global__ __launch_bounds__(kHhThreads) void hamming_hist_kernel(
+    const uint32_t* __restrict__ sigs, const uint32_t* __restrict__ qsig, int n, int n_cap, int lo,
+    int hi, int nseg, uint8_t* __restrict__ dist, uint32_t* __restrict__ ws) {
+  __shared__ uint32_t h[kHhWaves * 4][kHhBins];
+  const int seg = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
+  const uint32_t qs = qsig[row];
+  const uint32_t* srow = sigs + size_t(row) * n_cap;
+  uint8_t* drow = dist + size_t(row) * n;
+  if (seg == nseg) {
+    for (int i = tid; i < lo; i += kHhThreads) drow[i] = uint8_t(__popc(srow[i] ^ qs));
+    for (int i = hi + tid; i < n; i += kHhThreads) drow[i] = uint8_t(__popc(srow[i] ^ qs));
+    return;
+  }
+  const int copy = (tid >> 6) * 4 + (tid & 3);
+  for (int i = tid; i < kHhWaves * 4 * kHhBins; i += kHhThreads) (&h[0][0])[i] = 0;
+  const int s = lo + seg * kU8Seg + tid * kHhPer;
+  const int e = s + kHhPer < hi ? s + kHhPer : hi;
+  const int cnt = e > s ? e - s : 0;
+  uint32_t dw[kHhPer / 4];                                   // 4 distances per word
+  if (cnt == kHhPer && (reinterpret_cast<uintptr_t>(srow + s) & 15) == 0) {
+    const uint4* p = reinterpret_cast<const uint4*>(srow + s);
+    uint4 v[kHhPer / 4];
+#pragma unroll
+    for (int j = 0; j < kHhPer / 4; ++j) v[j] = p[j];
+#pragma unroll
+    for (int j = 0; j < kHhPer / 4; ++j)
+      dw[j] = uint32_t(__popc(v[j].x ^ qs)) | (uint32_t(__popc(v[j].y ^ qs)) << 8) |
+              (uint32_t(__popc(v[j].z ^ qs)) << 16) | (uint32_t(__popc(v[j].w ^ qs)) << 24);
+  } else {
+#pragma unroll
+    for (int j = 0; j < kHhPer / 4; ++j) {
+      uint32_t x = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int i = 4 * j + b;
+        if (i < cnt) x |= uint32_t(__popc(srow[s + i] ^ qs)) << (8 * b);
+      }
+      dw[j] = x;
+    }
+  }
+  if (cnt == kHhPer && (reinterpret_cast<uintptr_t>(drow + s) & 15) == 0) {
+    *reinterpret_cast<uint4*>(drow + s) = make_uint4(dw[0], dw[1], dw[2], dw[3]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kHhPer; ++i)
+      if (i < cnt) drow[s + i] = uint8_t((dw[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kHhPer; ++i)
+    if (i < cnt) atomicAdd(&h[copy][(dw[i >> 2] >> (8 * (i & 3))) & 0xFFu], 1u);
+  __syncthreads();
+  // each wave's four copies into its first, then the waves' sums per bin
+  if (tid < kHhWaves * kHhBins) {
+    const int w = tid / kHhBins, bin = tid - w * kHhBins;
+    h[4 * w][bin] += h[4 * w + 1][bin] + h[4 * w + 2][bin] + h[4 * w + 3][bin];
+  }
+  __syncthreads();
+  if (tid < 256) {
+    uint32_t t = 0;
+    if (tid < kHhBins) {
+#pragma unroll
+      for (int w = 0; w < kHhWaves; ++w) t += h[4 * w][tid];
+    }
+    ws[(size_t(row) * nseg + seg) * 256 + tid] = t;
+  }
+}
+
 __global__ __launch_bounds__(kU8SegThreads) void topk_u8_select_kernel(
     const uint8_t* __restrict__ keys, int n, int k, int n_sink, int n_local, int nseg,
     const uint32_t* __restrict__ ws, int32_t* __restrict__ out, int stride) {
@@ -1181,6 +1264,36 @@ extern "C" int topk_select(const void* keys, int key_type, int rows, int n, int 
     hipLaunchKernelGGL(topk_u8_kernel, dim3(rows), dim3(kTkThreads), 0, stream,
                        reinterpret_cast<const uint8_t*>(keys), n, k, n_sink, n_local, idx_out, stride);
   return check_launch("topk_select");
+}
+
+extern "C" int hamming_scan(const uint32_t* sigs, const uint32_t* qsig, int H, int n, int n_cap,
+                            uint8_t* dist, hipStream_t stream);
+
+extern "C" int hamming_scan_topk(const uint32_t* sigs, const uint32_t* qsig, int H, int n, int n_cap,
+                                 int k, int n_sink, int n_local, uint8_t* dist, int32_t* idx_out,
+                                 void* ws, size_t ws_bytes, hipStream_t stream) {
+  SDQ_REQUIRE(sigs && qsig && dist, "hamming_scan_topk: null pointer");
+  SDQ_REQUIRE(H >= 1 && n >= 1 && n <= n_cap, "hamming_scan_topk: H=%d, n=%d, n_cap=%d", H, n, n_cap);
+  int stride = 0;
+  const int rc = topk_validate("hamming_scan_topk", dist, SDQ_KEY_U8_MIN, H, n, k, n_sink, n_local,
+                               idx_out, &stride);
+  if (rc != SDQ_OK) return rc;
+  if (!use_u8_segments(n, n_sink, n_local, k) || stride == 0) {
+    const int r1 = hamming_scan(sigs, qsig, H, n, n_cap, dist, stream);
+    if (r1 != SDQ_OK) return r1;
+    return topk_select(dist, SDQ_KEY_U8_MIN, H, n, k, n_sink, n_local, idx_out, ws, ws_bytes, stream);
+  }
+  const size_t need_ws = topk_select_workspace_bytes(H, n, k, SDQ_KEY_U8_MIN);
+  SDQ_REQUIRE(ws && ws_bytes >= need_ws,
+              "hamming_scan_topk: workspace of %zu bytes needed, %zu given", need_ws, ws_bytes);
+  const int lo = n_sink, hi = n - n_local;
+  const int nseg = int(cdiv(size_t(hi - lo), kU8Seg));
+  uint32_t* hst = reinterpret_cast<uint32_t*>(ws);
+  hipLaunchKernelGGL(hamming_hist_kernel, dim3(nseg + 1, H), dim3(kHhThreads), 0, stream, sigs,
+                     qsig, n, n_cap, lo, hi, nseg, dist, hst);
+  hipLaunchKernelGGL(topk_u8_select_kernel, dim3(nseg, H), dim3(kU8SegThreads), 0, stream, dist, n,
+                     k, n_sink, n_local, nseg, hst, idx_out, stride);
+  return check_launch("hamming_scan_topk");
 }
 
 extern "C" int topk_select_block_max(const float* keys, const float* block_max, int rows, int n,

@@ -41,6 +41,8 @@ _SIGS = {
     "topk_select_workspace_bytes": ([_c_int, _c_int, _c_int, _c_int], _c_size),
     "topk_select": ([_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _c_size, _vp], _c_int),
     "hamming_scan": ([_vp, _vp, _c_int, _c_int, _c_int, _vp, _vp], _c_int),
+    "hamming_scan_topk": ([_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _c_size,
+                           _vp], _c_int),
     "minmax_block_scan": ([_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp], _c_int),
     "gather_attend_workspace_bytes": ([_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int], _c_size),
     "gather_attend": ([_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
@@ -349,6 +351,27 @@ def hamming_scan(sigs, qsig, dist=None, n=None, stream=None):
     _check(load().hamming_scan(_vp(sigs.data_ptr()), _vp(qsig.data_ptr()), H, n, n_cap,
                                _vp(dist.data_ptr()), _stream(stream)), "hamming_scan")
     return dist
+
+
+def hamming_scan_topk(sigs, qsig, k, n_sink=0, n_local=0, dist=None, idx=None, ws=None, n=None,
+                      stream=None):
+    """hamming_scan then the top-k smallest distances per row, in one call:
+    sigs uint32 [H][n_cap] (the first n scored), qsig uint32 [H] ->
+    (dist uint8 [H][n], idx int32 [H][n_sink + k + n_local])."""
+    H, n_cap = sigs.shape
+    n = n_cap if n is None else int(n)
+    _dev(sigs, "sigs", 4, H * n_cap)
+    _dev(qsig, "qsig", 4, H)
+    dist = _out(dist, (H, n), torch.uint8, sigs.device, "dist", 1)
+    idx = _out(idx, (H, int(n_sink) + int(k) + int(n_local)), torch.int32, sigs.device, "idx", 4)
+    if ws is None:
+        ws = topk_workspace(H, n, k, SDQ_KEY_U8_MIN, sigs.device)
+    _dev(ws, "ws", 1)
+    _check(load().hamming_scan_topk(_vp(sigs.data_ptr()), _vp(qsig.data_ptr()), H, n, n_cap, int(k),
+                                    int(n_sink), int(n_local), _vp(dist.data_ptr()),
+                                    _vp(idx.data_ptr()), _vp(ws.data_ptr()), ws.numel(),
+                                    _stream(stream)), "hamming_scan_topk")
+    return dist, idx
 
 
 def minmax_block_scan(bmin, bmax, q, scores=None, nb=None, stream=None):

@@ -68,6 +68,9 @@ def test_invalid_arguments_rejected_without_launch():
     assert L.topk_select(p, 0, 8, 1 << 20, 512, 0, 0, p, null, 0, s) == EINVAL   # no workspace
     assert L.hamming_scan(p, p, 0, 10, 10, p, s) == EINVAL
     assert L.hamming_scan(p, p, 4, 11, 10, p, s) == EINVAL                   # n > n_cap
+    assert L.hamming_scan_topk(p, p, 4, 11, 10, 2, 0, 0, p, p, p, 256, s) == EINVAL   # n > n_cap
+    assert L.hamming_scan_topk(p, p, 4, 10, 10, 2, 6, 5, p, p, p, 256, s) == EINVAL   # windows > n
+    assert L.hamming_scan_topk(p, p, 8, 1 << 20, 1 << 20, 512, 0, 0, p, p, null, 0, s) == EINVAL  # ws
     assert L.minmax_block_scan(p, p, p, 1, 4, 0, 8, 128, p, s) == EINVAL
     assert L.minmax_block_scan(p, p, p, 1, 4, 9, 8, 128, p, s) == EINVAL     # nb > nb_cap
     assert L.gather_attend(p, p, p, p, 1, 32, 6, 0, 100, 100, 8, 1, 128, 1.0, p, p, 1 << 20, s) == EINVAL

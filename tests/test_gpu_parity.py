@@ -322,6 +322,30 @@ def test_hamming_bitexact(sdq, H, n):
     assert np.array_equal(dist, o_hamming.distances_heads(sigs, case["qsig"]))
 
 
+@pytest.mark.parametrize("H,n,n_cap,k,ns,nl,kind", [
+    (32, 131072, 131072, 512, 128, 128, "case"),      # the config 4 shape, segmented
+    (3, 40001, 40017, 700, 3, 5, "case"),             # ragged n, odd capacity, unaligned rows
+    (2, 65536, 70000, 1, 0, 0, "case"),               # capacity past n, k = 1
+    (2, 70000, 70000, 5000, 0, 100, "const"),         # all distances tie
+    (2, 50000, 50000, 0, 16, 16, "case"),             # windows only: the two-call path
+    (3, 1000, 1024, 40, 0, 0, "case")])               # short rows: the two-call path
+def test_hamming_scan_topk_equals_oracle_and_separate_calls(sdq, H, n, n_cap, k, ns, nl, kind):
+    _say(f"hamming_scan_topk H={H} n={n} n_cap={n_cap} k={k} sink={ns} local={nl} {kind}")
+    case = synth.hamming_case(4, n=n_cap, H=H, with_kv=False)
+    sigs = case["sigs"].copy()
+    if kind == "const":
+        sigs[:] = case["qsig"][:, None] ^ np.uint32(0x0F0F)
+    sig_d, q_d = dev(sigs), dev(case["qsig"])
+    dist, idx = sdq.hamming_scan_topk(sig_d, q_d, k, ns, nl, n=n)
+    dist2 = sdq.hamming_scan(sig_d, q_d, n=n)
+    idx2 = sdq.topk_select(dist2, k, ns, nl)
+    torch.cuda.synchronize()
+    rdist = o_hamming.distances_heads(sigs[:, :n], case["qsig"])
+    assert np.array_equal(host(dist), rdist)
+    assert np.array_equal(host(idx), _topk_ref(rdist, k, ns, nl, False))
+    assert np.array_equal(host(idx), host(idx2))
+
+
 # ---------------------------------------------------------------- min/max summaries
 def test_minmax_parity(sdq):
     _say("minmax summaries + block scores")
