@@ -318,13 +318,7 @@ def main():
         extras = run_extras(torch, np, lib, bytemodel, synth, dev, case, K4, V4, q, var, q3, index,
                             P, M, n, G, Hgrp, k)
     if args.copy_calibration:
-        # a plain elementwise copy of known size (multiply by one: 512 MiB read, 512 MiB written)
-        src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(4):
-            torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        extras["copy_calibration_bytes"] = src.numel() * 4
+        extras["copy_calibration_bytes"] = copy_calibration(torch, dev)
 
     cpu = cpu_all = None
     if not args.no_cpu:
@@ -656,6 +650,17 @@ def variant_minmax(torch, np, lib, bytemodel, synth, dev, timeit):
     return us_step, us_scan, info
 
 
+def copy_calibration(torch, dev):
+    """A plain elementwise copy of known size (multiply by one: 512 MiB read,
+    512 MiB written), for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    return src.numel() * 4
+
+
 def run_variant(args):
     """--variant hamming|minmax|oasis: only that step, W warm-up + K steps (the
     resident-pool step fills its pool first, untimed, and times K steps), for
@@ -683,8 +688,11 @@ def run_variant(args):
         step(i)
     e1.record()
     torch.cuda.synchronize()
-    print(json.dumps({"variant": args.variant, "steps": args.steps,
-                      "us_per_step": round(e0.elapsed_time(e1) / args.steps * 1e3, 2)}), flush=True)
+    line = {"variant": args.variant, "steps": args.steps,
+            "us_per_step": round(e0.elapsed_time(e1) / args.steps * 1e3, 2)}
+    if args.copy_calibration:
+        line["copy_calibration_bytes"] = copy_calibration(torch, dev)
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

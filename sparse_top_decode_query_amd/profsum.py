@@ -70,7 +70,8 @@ def counter_per_dispatch(db_path, counter, name_filter):
     return statistics.mean(per.values()), len(per)
 
 
-def traffic_summary(fetch_db, write_db, kernel, copy_bytes, plan_sha, cmd_fetch, cmd_write):
+def traffic_summary(fetch_db, write_db, kernel, copy_bytes, plan_sha, cmd_fetch, cmd_write,
+                    source=SCAN_SOURCE):
     copy_tag = "MulFunctor"
     f_k, nf = counter_per_dispatch(fetch_db, "FETCH_SIZE", kernel)
     w_k, nw = counter_per_dispatch(write_db, "WRITE_SIZE", kernel)
@@ -80,8 +81,10 @@ def traffic_summary(fetch_db, write_db, kernel, copy_bytes, plan_sha, cmd_fetch,
     sw = copy_bytes / (w_c * 1024.0)
     fetch_b = f_k * 1024.0 * sf
     write_b = w_k * 1024.0 * sw
-    with open(SCAN_SOURCE, "rb") as f:
+    with open(source, "rb") as f:
         src_sha = hashlib.sha256(f.read()).hexdigest()
+    sha_key = "scan_source_sha256" if os.path.abspath(source) == os.path.abspath(SCAN_SOURCE) \
+        else f"source_sha256 ({os.path.relpath(source, _PKG)})"
     return "\n".join([
         f"# HBM traffic of {kernel} per dispatch (rocprofv3 --pmc, two runs)",
         f"command_fetch: {cmd_fetch}",
@@ -99,7 +102,7 @@ def traffic_summary(fetch_db, write_db, kernel, copy_bytes, plan_sha, cmd_fetch,
         f"fetch_bytes_per_launch: {fetch_b:.0f}",
         f"write_bytes_per_launch: {write_b:.0f}",
         f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}",
-        f"scan_source_sha256: {src_sha}",
+        f"{sha_key}: {src_sha}",
         f"plan_sha256: {plan_sha}",
     ]) + "\n"
 
@@ -144,7 +147,8 @@ def main(argv=None):
     b.add_argument("out")
     b.add_argument("--kernel", default="fathom_scan")
     b.add_argument("--copy-bytes", type=int, required=True)
-    b.add_argument("--plan-sha256", required=True)
+    b.add_argument("--plan-sha256", default="-", help="sha256 of the plan the scan ran (scan only)")
+    b.add_argument("--source", default="scan.hip", help="the kernel's source file under csrc/")
     b.add_argument("--command-fetch", required=True)
     b.add_argument("--command-write", required=True)
     c = sub.add_parser("counters")
@@ -160,7 +164,8 @@ def main(argv=None):
         text = counters_summary(args.dbs, args.kernel, args.command, args.clocks)
     else:
         text = traffic_summary(args.fetch_db, args.write_db, args.kernel, args.copy_bytes,
-                               args.plan_sha256, args.command_fetch, args.command_write)
+                               args.plan_sha256, args.command_fetch, args.command_write,
+                               os.path.join(_PKG, "csrc", args.source))
     with open(args.out, "w") as f:
         f.write(text)
     print(text, end="")
