@@ -744,11 +744,21 @@ __global__ __launch_bounds__(kU8SegThreads) void topk_u8_select_kernel(
   if (seg == 0) write_fixed(o, n, n_sink, n_local, K, stride);
   // thread d: distance d's count over the row and over the segments before this one
   const uint32_t* hr = ws + size_t(row) * nseg * 256;
+  // eight loads in flight per batch (clamped indices keep them unconditional)
   int tot = 0, before = 0;
-  for (int s0 = 0; s0 < nseg; ++s0) {
-    const int c = int(hr[size_t(s0) * 256 + tid]);
-    tot += c;
-    if (s0 < seg) before += c;
+  for (int s0 = 0; s0 < nseg; s0 += 8) {
+    uint32_t c[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int sg = s0 + u < nseg ? s0 + u : nseg - 1;
+      c[u] = hr[size_t(sg) * 256 + tid];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int v = s0 + u < nseg ? int(c[u]) : 0;
+      tot += v;
+      if (s0 + u < seg) before += v;
+    }
   }
   // T: smallest d with (count of keys <= d) >= K; prefix over d = tid
   int inc = wave_incl_scan(tot);
