@@ -96,3 +96,33 @@ def test_gather_attend_at_maximum_length(sdq):
         assert float(np.abs(O[0, h] - ref).max()) <= 2e-2
     del K, V
     torch.cuda.empty_cache()
+
+
+def test_hamming_scan_topk_at_large_length(sdq):
+    """2 rows of n = 2^25 + 12345 signatures (2049 segments per row, ragged
+    tail): the distances equal the oracle's, and the selection is the unique
+    one (every competition distance below the k-th, then the lowest-index
+    ties), checked from the oracle's distances without a full sort."""
+    from oracle import hamming as o_hamming
+    H, n, k, ns, nl = 2, (1 << 25) + 12345, 2048, 64, 64
+    _say(f"hamming_scan_topk H={H} n={n} k={k}")
+    g = np.random.default_rng(94)
+    sigs = g.integers(0, 1 << 32, size=(H, n), dtype=np.uint64).astype(np.uint32)
+    qsig = g.integers(0, 1 << 32, size=H, dtype=np.uint64).astype(np.uint32)
+    dist, idx = sdq.hamming_scan_topk(torch.from_numpy(sigs.view(np.int32)).cuda(),
+                                      torch.from_numpy(qsig.view(np.int32)).cuda(), k, ns, nl)
+    torch.cuda.synchronize()
+    rd = o_hamming.distances_heads(sigs, qsig)
+    assert np.array_equal(dist.cpu().numpy(), rd)
+    got = idx.cpu().numpy()
+    for h in range(H):
+        comp = rd[h, ns:n - nl]
+        cnt = np.bincount(comp, minlength=33)
+        T = int(np.searchsorted(np.cumsum(cnt), k))      # smallest d with count(<= d) >= k
+        below = int(cnt[:T].sum())
+        ties = np.flatnonzero(comp == T)[:k - below] + ns
+        want = np.sort(np.concatenate([np.arange(ns), np.flatnonzero(comp < T) + ns, ties,
+                                       np.arange(n - nl, n)]))
+        assert np.array_equal(got[h], want)
+    del dist, idx
+    torch.cuda.empty_cache()
