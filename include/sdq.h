@@ -139,7 +139,8 @@ int minmax_append(const uint16_t* keys, int RG, int d, int n_cap, int n_old, int
  * share one plan.
  *   q        float32 [G*H_grp][d]  query rows; rows g*H_grp..g*H_grp+H_grp-1
  *            belong to KV head g
- *   key_var  float32 [G][d]        calibrated key variance per channel (>= 0)
+ *   key_var  float32 [G][d]        calibrated key variance per channel (>= 0;
+ *            a weight that comes out negative or NaN is read as zero gain)
  *   depth    uint8 [G][d]   out: bits to read per channel (0..4)
  *   qbar     float32 [G][d] out: the group's query sum, added in head order
  * Exactly min(budget_bits, 4d) bits are given out per KV head: the items

@@ -176,9 +176,14 @@ def group_query(q_grp: np.ndarray) -> np.ndarray:
 
 
 def channel_weight(qbar: np.ndarray, var: np.ndarray) -> np.ndarray:
-    """w_j = (qbar_j * qbar_j) * var_j, two float32 multiplies."""
+    """w_j = (qbar_j * qbar_j) * var_j, two float32 multiplies.
+
+    A variance is never negative, so a weight that comes out negative or NaN
+    (a negative or NaN variance handed in) is read as zero gain: that channel
+    competes only for bits nobody else wants, in channel order."""
     qq = (qbar.astype(np.float32) * qbar.astype(np.float32)).astype(np.float32)
-    return (qq * np.asarray(var, np.float32)).astype(np.float32)
+    w = (qq * np.asarray(var, np.float32)).astype(np.float32)
+    return np.where(w > 0, w, np.float32(0)).astype(np.float32)
 
 
 def plan(q_grp: np.ndarray, var: np.ndarray, budget: int):

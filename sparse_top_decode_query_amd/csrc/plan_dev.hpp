@@ -63,9 +63,14 @@ __device__ __forceinline__ HeadPlan plan_head(const float* __restrict__ q,
       a1 = h0 + k == 0 ? r1[k] : (in ? s1 : a1);
     }
   }
-  // w = (qbar*qbar)*var as two rounded multiplies; -0 folded onto +0
-  const float w0 = __fadd_rn(__fmul_rn(__fmul_rn(a0, a0), va0), 0.0f);
-  const float w1 = __fadd_rn(__fmul_rn(__fmul_rn(a1, a1), va1), 0.0f);
+  // w = (qbar*qbar)*var as two rounded multiplies.  A variance is never
+  // negative: a weight that is negative, -0 or NaN (a bad variance handed in)
+  // is read as +0, so every gain's exponent field indexes the 256-bin
+  // histogram below.
+  float w0 = __fmul_rn(__fmul_rn(a0, a0), va0);
+  float w1 = __fmul_rn(__fmul_rn(a1, a1), va1);
+  w0 = w0 > 0.0f ? w0 : 0.0f;
+  w1 = w1 > 0.0f ? w1 : 0.0f;
 
   constexpr int NT = UNIFORM ? 1 : 4;      // candidate bits per channel
   const float step[4] = {1.0f, 0.25f, 0.0625f, 0.015625f};

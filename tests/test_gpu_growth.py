@@ -279,6 +279,11 @@ def test_minmax_append_and_capacity_scan(sdq):
 
 
 def test_fathom_gather_capacity_prefix(sdq):
+    """Gather from a capacity row that holds n < n_cap tokens: the staged
+    prefixes equal the oracle's index of the first n tokens (closed blocks
+    final, the open block quantised over its present tokens), everything
+    else keeps its sentinel, and the staged copy scores within tolerance of
+    the oracle."""
     G, n_cap, n = 2, 2048, 1000
     _say(f"fathom_gather n={n} of n_cap={n_cap}")
     case = synth.fathom_case(2, n=n_cap, heads=[0, 1], with_values=False)
@@ -292,17 +297,25 @@ def test_fathom_gather_capacity_prefix(sdq):
     s_off = sdq.fathom_scan(index, depth, qbar, n, planes=pd, meta=md)
     s_on = sdq.fathom_scan(index, depth, qbar, n)
     torch.cuda.synchronize()
+    rp, rm = o_fathom.ingest(case["K"], n, n_cap)
+    rd, rq = o_fathom.plan_heads(case["q"][:8], case["var"][:2], 4, budget=56)
     d = host(depth)
-    P, Pd = host(index.planes, np.uint32), host(pd, np.uint32)
-    M, Md = host(index.meta, np.uint32), host(md, np.uint32)
+    assert np.array_equal(d, rd)
+    Pd, Md = host(pd, np.uint32), host(md, np.uint32)
     w, b = _r64(n) // 32, _r64(n) // 64
     for g in range(G):
         for j in range(128):
             t = int(d[g, j])
-            assert np.array_equal(Pd[g, j, :t, :w], P[g, j, :t, :w])
+            assert np.array_equal(Pd[g, j, :t, :w], rp[g, j, :t, :w])
             assert np.all(Pd[g, j, :t, w:] == SENTINEL) and np.all(Pd[g, j, t:] == SENTINEL)
             if t:
-                assert np.array_equal(Md[g, j, :b], M[g, j, :b]) and np.all(Md[g, j, b:] == SENTINEL)
+                assert np.array_equal(Md[g, j, :b], rm[g, j, :b]) and np.all(Md[g, j, b:] == SENTINEL)
             else:
                 assert np.all(Md[g, j] == SENTINEL)
+    S = host(s_off)
+    for g in range(G):
+        ref = o_fathom.scan(rp[g], rm[g], rd[g], rq[g], n)
+        rng = float(ref.max() - ref.min())
+        assert float(np.abs(S[g, :n].astype(np.float64) - ref).max()) <= SCORE_RTOL * rng + 1e-6
+        assert np.all(np.isneginf(S[g, n:]))
     assert torch.equal(s_off, s_on)

@@ -593,3 +593,86 @@ def test_oasis_fetch_copies_planned_blocks():
     out = oasis.fetch(pool, host, [(1, 6), (3, 4)])
     assert np.array_equal(out[1], host[6]) and np.array_equal(out[3], host[4])
     assert not out[0].any() and not out[2].any()
+
+
+# ---------------------------------------------------------------- plan: tie order and bad gains
+def test_plan_uniform_ties_go_to_the_lower_channel():
+    """Equal weights everywhere: the uniform plan must keep the lowest
+    channels.  A plan that broke ties toward the higher channel, or by sort
+    instability, would pick another set."""
+    q = np.ones((4, 128), np.float32)
+    var = np.full(128, 0.5, np.float32)
+    dep, _ = fathom.plan_uniform(q, var, 34)
+    assert dep[:34].tolist() == [4] * 34 and not dep[34:].any()
+    # 28 strictly larger channels at the top of the range, then a tie among
+    # the rest: the 6 remaining slots go to channels 0..5
+    var2 = var.copy()
+    var2[100:] = 2.0
+    dep2, _ = fathom.plan_uniform(q, var2, 34)
+    assert np.flatnonzero(dep2).tolist() == list(range(6)) + list(range(100, 128))
+    assert set(dep2.tolist()) == {0, 4}
+
+
+def test_plan_greedy_ties_go_to_the_lower_channel():
+    """Equal weights and B = 3d/2: every channel gets its first bit (gain w),
+    then the half budget left goes to the second bits (gain w/4) of the
+    lowest 64 channels."""
+    q = np.ones((4, 128), np.float32)
+    var = np.full(128, 0.5, np.float32)
+    dep, _ = fathom.plan(q, var, 192)
+    assert dep[:64].tolist() == [2] * 64 and dep[64:].tolist() == [1] * 64
+
+
+def test_plan_negative_or_nan_variance_reads_as_zero_gain():
+    """A variance is never negative: a negative or NaN variance gives the
+    channel zero gain, so it is planned exactly like a zero variance and
+    never ahead of a channel with positive gain."""
+    g = np.random.default_rng(31)
+    q = g.standard_normal((4, 128)).astype(np.float32)
+    var = g.uniform(0.01, 4, 128).astype(np.float32)
+    bad = var.copy()
+    bad[[3, 40, 77]] = [-1.0, np.nan, -np.inf]
+    zero = var.copy()
+    zero[[3, 40, 77]] = 0.0
+    for B in (0, 56, 400, 500, 512):
+        assert np.array_equal(fathom.plan(q, bad, B)[0], fathom.plan(q, zero, B)[0])
+    # with all 125 good channels full (500 bits), 12 more bits go to the
+    # zero-gain channels in channel order: 4 each to channels 3, 40, 77
+    d512 = fathom.plan(q, bad, 512)[0]
+    assert d512.tolist() == [4] * 128
+    d500 = fathom.plan(q, bad, 500)[0]
+    assert d500[[3, 40, 77]].tolist() == [0, 0, 0] and int(d500.sum()) == 500
+    assert fathom.plan_uniform(q, bad, 126)[0][[3, 40]].tolist() == [4, 0]
+
+
+# ---------------------------------------------------------------- attention: logit shift
+def test_attend_invariant_under_a_common_logit_shift():
+    """Adding the same constant to every logit leaves the output unchanged.
+    With a query that is zero outside channel 0, adding delta to channel 0 of
+    every key (exact in bf16 while |k| < 256) adds q_0 * delta / sqrt(d) to
+    every logit.  With q_0 = 64 and delta = 200 the logits pass 1100, where
+    an unnormalised exp overflows float64, so this also pins the maximum
+    subtraction."""
+    g = np.random.default_rng(33)
+    n, d = 40, 128
+    k0 = g.integers(-8, 9, n).astype(np.float32)
+    Krest = g.standard_normal((n, d)).astype(np.float32)
+    Vb = _bf16(g.standard_normal((n, d)))
+    for q0 in (0.75, 64.0):
+        q = np.zeros(d, np.float32)
+        q[0] = q0
+        outs = []
+        for delta in (0.0, 3.0, -5.0, 200.0):
+            K = Krest.copy()
+            K[:, 0] = k0 + np.float32(delta)
+            Kb = _bf16(K)
+            assert np.array_equal(attend.bf16_bits_to_f64(Kb)[:, 0], (k0 + delta).astype(np.float64))
+            outs.append(attend.attend_rows(q, Kb, Vb, 1 / math.sqrt(d)))
+        for o in outs[1:]:
+            assert np.all(np.isfinite(o))
+            assert np.allclose(o, outs[0], rtol=1e-9, atol=1e-12)
+        # the common value is the softmax of q_0 * k0 / sqrt(d) weighting V
+        z = q0 * k0.astype(np.float64) / math.sqrt(d)
+        p = np.exp(z - z.max())
+        ref = (p / p.sum()) @ attend.bf16_bits_to_f64(Vb)
+        assert np.allclose(outs[0], ref, rtol=1e-9, atol=1e-12)
