@@ -25,8 +25,10 @@
  *       SDQ_ENOTSUP (-2), SDQ_EHIP (-3: a HIP launch/runtime error).
  *     sdq_last_error() returns a message for the calling thread's last error.
  *   - The library holds no global mutable state apart from that per-thread
- *     message; calls on different streams may run concurrently if their
- *     output and workspace buffers do not overlap.
+ *     message and the static per-GPU scratch of topk_select_noalloc; calls
+ *     on different streams may run concurrently if their output and
+ *     workspace buffers do not overlap (topk_select_noalloc calls on one GPU
+ *     share their scratch and must not overlap).
  *   - Head dimension d must be 128 in this version.
  *   - bf16 and fp16 data are passed as uint16_t bit patterns.
  */
@@ -244,6 +246,24 @@ int fathom_plan_scan(const float* q, const float* key_var, int H_grp, int budget
 size_t topk_select_workspace_bytes(int rows, int n, int k, int key_type);
 int topk_select(const void* keys, int key_type, int rows, int n, int k, int n_sink, int n_local,
                 int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* topk_select_noalloc -- topk_select without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  It calls no
+ * allocating routine.  Its scratch is one static device array of
+ * SDQ_TOPK_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends; the
+ * first call on a device looks up that device's copy.  Every call on a GPU
+ * shares that GPU's array, so calls that overlap on one GPU (other streams,
+ * other threads) race and must be ordered by the caller.  Its contents on
+ * entry do not matter (what must start at zero is cleared by a kernel).
+ * Arguments, ordering, windows and output are those of topk_select.
+ * Errors: those of topk_select; SDQ_EINVAL when
+ * topk_select_workspace_bytes(rows, n, k, key_type) exceeds
+ * SDQ_TOPK_NOALLOC_SCRATCH_BYTES (nothing is launched); SDQ_EHIP when the
+ * scratch cannot be looked up on the current device. */
+#define SDQ_TOPK_NOALLOC_SCRATCH_BYTES (16u << 20)
+int topk_select_noalloc(const void* keys, int key_type, int rows, int n, int k, int n_sink,
+                        int n_local, int32_t* idx_out, hipStream_t stream);
 
 /* topk_select_block_max -- topk_select for float32 scores whose 64-key
  * block maxima are already known (fathom_scan writes them).  Same ordering,

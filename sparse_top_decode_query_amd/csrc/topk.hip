@@ -28,6 +28,8 @@
 //    the row path.
 #include "common.hpp"
 
+#include <mutex>
+
 namespace sdq {
 
 constexpr int kTkThreads = 512;
@@ -1220,29 +1222,27 @@ static void launch_block_max_select(const float* fk, const float* bm, int rows, 
                      n_sink, n_local, idx_out, stride);
 }
 
-extern "C" int topk_select(const void* keys, int key_type, int rows, int n, int k, int n_sink,
-                           int n_local, int32_t* idx_out, void* ws, size_t ws_bytes,
-                           hipStream_t stream) {
-  int stride = 0;
-  const int rc = topk_validate("topk_select", keys, key_type, rows, n, k, n_sink, n_local, idx_out,
-                               &stride);
-  if (rc != SDQ_OK) return rc;
-  if (stride == 0) return SDQ_OK;
+// topk_select's launches over a given scratch buffer (the caller's workspace,
+// or the library's static one for topk_select_noalloc).  Arguments are
+// already validated; stride = k + n_sink + n_local > 0.
+static int topk_select_launch(const char* nm, const void* keys, int key_type, int rows, int n, int k,
+                              int n_sink, int n_local, int32_t* idx_out, int stride, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
   const size_t need_ws = topk_select_workspace_bytes(rows, n, k, key_type);
   const float* fk = reinterpret_cast<const float*>(keys);
   if (use_block_max(n, n_sink, n_local, k, key_type) &&
       reinterpret_cast<uintptr_t>(keys) % 16 == 0) {
-    SDQ_REQUIRE(ws && ws_bytes >= need_ws, "topk_select: workspace of %zu bytes needed, %zu given",
+    SDQ_REQUIRE(ws && ws_bytes >= need_ws, "%s: workspace of %zu bytes needed, %zu given", nm,
                 need_ws, ws_bytes);
     float* bm = reinterpret_cast<float*>(ws);
     const int nb = n / 64;
     hipLaunchKernelGGL(topk_block_max_kernel, dim3(cdiv(nb, 4), rows), dim3(256), 0, stream, fk, n,
                        nb, bm);
     launch_block_max_select(fk, bm, rows, n, k, n_sink, n_local, idx_out, stride, stream);
-    return check_launch("topk_select");
+    return check_launch(nm);
   }
   if (use_fast(n, n_sink, n_local, k, key_type)) {
-    SDQ_REQUIRE(ws && ws_bytes >= need_ws, "topk_select: workspace of %zu bytes needed, %zu given",
+    SDQ_REQUIRE(ws && ws_bytes >= need_ws, "%s: workspace of %zu bytes needed, %zu given", nm,
                 need_ws, ws_bytes);
     const int lo = n_sink, hi = n - n_local;
     dim3 g2(cdiv(hi - lo, kFastChunk), rows);
@@ -1252,10 +1252,10 @@ extern "C" int topk_select(const void* keys, int key_type, int rows, int n, int 
     hipLaunchKernelGGL(topk_collect_kernel, g2, dim3(256), 0, stream, fk, n, lo, hi, ws);
     hipLaunchKernelGGL(topk_final_kernel, dim3(rows), dim3(kTkThreads), 0, stream, fk, n, k, n_sink,
                        n_local, ws, idx_out, stride);
-    return check_launch("topk_select");
+    return check_launch(nm);
   }
   if (key_type == SDQ_KEY_U8_MIN && use_u8_segments(n, n_sink, n_local, k)) {
-    SDQ_REQUIRE(ws && ws_bytes >= need_ws, "topk_select: workspace of %zu bytes needed, %zu given",
+    SDQ_REQUIRE(ws && ws_bytes >= need_ws, "%s: workspace of %zu bytes needed, %zu given", nm,
                 need_ws, ws_bytes);
     const int lo = n_sink, hi = n - n_local;
     const int nseg = int(cdiv(size_t(hi - lo), kU8Seg));
@@ -1265,7 +1265,7 @@ extern "C" int topk_select(const void* keys, int key_type, int rows, int n, int 
                        lo, hi, nseg, h);
     hipLaunchKernelGGL(topk_u8_select_kernel, dim3(nseg, rows), dim3(kU8SegThreads), 0, stream, u8,
                        n, k, n_sink, n_local, nseg, h, idx_out, stride);
-    return check_launch("topk_select");
+    return check_launch(nm);
   }
   if (key_type == SDQ_KEY_F32_MAX)
     hipLaunchKernelGGL(topk_row_kernel<SDQ_KEY_F32_MAX>, dim3(rows), dim3(kTkThreads), 0, stream,
@@ -1273,7 +1273,81 @@ extern "C" int topk_select(const void* keys, int key_type, int rows, int n, int 
   else
     hipLaunchKernelGGL(topk_u8_kernel, dim3(rows), dim3(kTkThreads), 0, stream,
                        reinterpret_cast<const uint8_t*>(keys), n, k, n_sink, n_local, idx_out, stride);
-  return check_launch("topk_select");
+  return check_launch(nm);
+}
+
+
+extern "C" int topk_select(const void* keys, int key_type, int rows, int n, int k, int n_sink,
+                           int n_local, int32_t* idx_out, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  int stride = 0;
+  const int rc = topk_validate("topk_select", keys, key_type, rows, n, k, n_sink, n_local, idx_out,
+                               &stride);
+  if (rc != SDQ_OK) return rc;
+  if (stride == 0) return SDQ_OK;
+  return topk_select_launch("topk_select", keys, key_type, rows, n, k, n_sink, n_local, idx_out,
+                            stride, ws, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------- no-allocation variant
+// The scratch of topk_select_noalloc: one static array per GPU the library
+// runs on, held until the process ends.  Host code never uses its name as an
+// address (on the host it is only a stand-in for the symbol): the device
+// address of each GPU's copy comes from hipGetSymbolAddress, once per device,
+// and is what the kernels receive.
+static __device__ __align__(256) uint8_t scratch[SDQ_TOPK_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+// Device address of the current device's scratch, looked up on the first call
+// on that device.  Returns SDQ_OK or SDQ_EHIP (message recorded).
+static int noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    set_error("topk_select_noalloc: hipGetDevice failed: %s", hipGetErrorString(e));
+    return SDQ_EHIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    set_error("topk_select_noalloc: device %d beyond the %d supported", dev, kMaxDevices);
+    return SDQ_EHIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      set_error("topk_select_noalloc: hipGetSymbolAddress of the scratch failed on device %d: %s",
+                dev, hipGetErrorString(e));
+      return SDQ_EHIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SDQ_OK;
+}
+
+extern "C" int topk_select_noalloc(const void* keys, int key_type, int rows, int n, int k,
+                                   int n_sink, int n_local, int32_t* idx_out, hipStream_t stream) {
+  int stride = 0;
+  const int rc = topk_validate("topk_select_noalloc", keys, key_type, rows, n, k, n_sink, n_local,
+                               idx_out, &stride);
+  if (rc != SDQ_OK) return rc;
+  const size_t need = topk_select_workspace_bytes(rows, n, k, key_type);
+  SDQ_REQUIRE(need <= size_t(SDQ_TOPK_NOALLOC_SCRATCH_BYTES),
+              "topk_select_noalloc: rows=%d x n=%d needs %zu bytes of scratch, the static scratch "
+              "holds %zu (use topk_select with a workspace)",
+              rows, n, need, size_t(SDQ_TOPK_NOALLOC_SCRATCH_BYTES));
+  if (stride == 0) return SDQ_OK;
+  void* ws = nullptr;
+  const int rs = noalloc_scratch(&ws);
+  if (rs != SDQ_OK) return rs;
+  return topk_select_launch("topk_select_noalloc", keys, key_type, rows, n, k, n_sink, n_local,
+                            idx_out, stride, ws, size_t(SDQ_TOPK_NOALLOC_SCRATCH_BYTES), stream);
 }
 
 extern "C" int hamming_scan(const uint32_t* sigs, const uint32_t* qsig, int H, int n, int n_cap,

@@ -40,6 +40,7 @@ _SIGS = {
     "topk_select_block_max": ([_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp], _c_int),
     "topk_select_workspace_bytes": ([_c_int, _c_int, _c_int, _c_int], _c_size),
     "topk_select": ([_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _c_size, _vp], _c_int),
+    "topk_select_noalloc": ([_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp], _c_int),
     "hamming_scan": ([_vp, _vp, _c_int, _c_int, _c_int, _vp, _vp], _c_int),
     "hamming_scan_topk": ([_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _c_size,
                            _vp], _c_int),
@@ -337,6 +338,27 @@ def topk_select(keys, k, n_sink=0, n_local=0, idx=None, ws=None, stream=None):
     _check(load().topk_select(_vp(keys.data_ptr()), kt, rows, n, int(k), int(n_sink), int(n_local),
                               _vp(idx.data_ptr()), _vp(ws.data_ptr()), ws.numel(), _stream(stream)),
            "topk_select")
+    return idx
+
+
+def topk_select_noalloc(keys, k, n_sink=0, n_local=0, idx=None, stream=None):
+    """topk_select on the library's static scratch (no workspace argument):
+    keys float32 (largest first) or uint8 (smallest first) [rows][n] ->
+    idx int32 [rows][k + n_sink + n_local].  Pass ``idx`` to allocate nothing
+    at all; calls that overlap on one GPU share the scratch and race."""
+    rows, n = keys.shape
+    if keys.dtype == torch.float32:
+        kt = SDQ_KEY_F32_MAX
+        _dev(keys, "keys", 4, rows * n)
+    elif keys.dtype == torch.uint8:
+        kt = SDQ_KEY_U8_MIN
+        _dev(keys, "keys", 1, rows * n)
+    else:
+        raise SDQError("keys must be float32 or uint8")
+    idx = _out(idx, (rows, k + n_sink + n_local), torch.int32, keys.device, "idx", 4)
+    _check(load().topk_select_noalloc(_vp(keys.data_ptr()), kt, rows, n, int(k), int(n_sink),
+                                      int(n_local), _vp(idx.data_ptr()), _stream(stream)),
+           "topk_select_noalloc")
     return idx
 
 

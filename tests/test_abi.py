@@ -66,6 +66,9 @@ def test_invalid_arguments_rejected_without_launch():
     assert L.topk_select(p, 7, 1, 10, 2, 0, 0, p, p, 256, s) == EINVAL       # key type
     assert L.topk_select(p, 0, 1, 10, 2, 6, 5, p, p, 256, s) == EINVAL       # windows > n
     assert L.topk_select(p, 0, 8, 1 << 20, 512, 0, 0, p, null, 0, s) == EINVAL   # no workspace
+    assert L.topk_select_noalloc(p, 0, 512, 1 << 20, 512, 0, 0, p, s) == EINVAL  # beyond the scratch
+    assert b"static scratch" in L.sdq_last_error()
+    assert L.topk_select_noalloc(p, 7, 1, 10, 2, 0, 0, p, s) == EINVAL             # key type
     assert L.hamming_scan(p, p, 0, 10, 10, p, s) == EINVAL
     assert L.hamming_scan(p, p, 4, 11, 10, p, s) == EINVAL                   # n > n_cap
     assert L.hamming_scan_topk(p, p, 4, 11, 10, 2, 0, 0, p, p, p, 256, s) == EINVAL   # n > n_cap
