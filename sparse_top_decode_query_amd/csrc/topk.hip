@@ -259,6 +259,98 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const void* __rest
   topk_row<KT>(keys, size_t(row) * n, n, k, n_sink, n_local, out + size_t(row) * stride, stride);
 }
 
+// Rows short enough to sit in LDS (float32, at most kRowLdsMax competing
+// keys): the row's order-preserving codes are read from memory once, every
+// load in flight together, and the selection passes and the ordered write
+// then read LDS instead of memory.  Same ordering and output as topk_row.
+constexpr int kRowLdsMax = 32768;
+
+__global__ __launch_bounds__(kTkThreads) void topk_row_lds_kernel(const float* __restrict__ keys,
+                                                                  int n, int k, int n_sink,
+                                                                  int n_local,
+                                                                  int32_t* __restrict__ out,
+                                                                  int stride) {
+  __shared__ uint32_t s_code[kRowLdsMax];
+  __shared__ uint32_t hist[256];
+  __shared__ int s_scan[2 * kTkWaves];
+  __shared__ uint32_t s_red[2 * kTkWaves];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  int32_t* o = out + size_t(row) * stride;
+  const int lo = n_sink, hi = n - n_local, m = hi - lo;
+  const int K = k < m ? k : m;
+  write_fixed(o, n, n_sink, n_local, K, stride);
+  if (K == m) {
+    for (int i = tid; i < m; i += kTkThreads) o[n_sink + i] = lo + i;
+    return;
+  }
+  if (K == 0) return;
+  const float* src = keys + size_t(row) * n + lo;
+  constexpr int LPT = 16;                      // loads per thread issued together
+  for (int c0 = 0; c0 < m; c0 += kTkThreads * LPT) {
+    float v[LPT];
+#pragma unroll
+    for (int e = 0; e < LPT; ++e) {
+      const int i = c0 + e * kTkThreads + tid;
+      v[e] = i < m ? src[i] : 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < LPT; ++e) {
+      const int i = c0 + e * kTkThreads + tid;
+      if (i < m) s_code[i] = f32_order_key(v[e]);
+    }
+  }
+  __syncthreads();
+  const KthResult kr = select_kth(
+      m, K,
+      [&](int i, uint32_t* u) {
+        *u = s_code[i];
+        return true;
+      },
+      hist, s_red);
+  const uint32_t T = kr.T;
+  const int need = kr.need;
+  constexpr int IPT = 8;
+  int out_pos = n_sink, eq_seen = 0;
+  for (int c0 = 0; c0 < m; c0 += kTkThreads * IPT) {
+    const int i0 = c0 + tid * IPT;
+    uint32_t u[IPT];
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int e = 0; e < IPT; ++e) {
+      const int i = i0 + e;
+      u[e] = i < m ? s_code[i] : 0u;
+      if (i < m) {
+        gt += u[e] > T;
+        eq += u[e] == T;
+      }
+    }
+    int egt, eeq, tgt, teq;
+    block_scan2(gt, eq, egt, eeq, tgt, teq, s_scan);
+    const int eq_left = need - eq_seen > 0 ? need - eq_seen : 0;
+    int pos = out_pos + egt + (eeq < eq_left ? eeq : eq_left);
+    int my_eq = eeq;
+    const int end = n_sink + K;
+#pragma unroll
+    for (int e = 0; e < IPT; ++e) {
+      const int i = i0 + e;
+      if (i < m) {
+        if (u[e] > T) {
+          if (pos < end) o[pos] = lo + i;
+          ++pos;
+        } else if (u[e] == T) {
+          if (my_eq < eq_left) {
+            if (pos < end) o[pos] = lo + i;
+            ++pos;
+          }
+          ++my_eq;
+        }
+      }
+    }
+    out_pos += tgt + (teq < eq_left ? teq : eq_left);
+    eq_seen += teq;
+  }
+}
+
 // ------------------------------------------------------------- fast path
 __device__ __forceinline__ uint32_t* ws_hist(void* ws, int row) {
   return reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws) + size_t(row) * fast_ws_per_row());
@@ -1267,7 +1359,10 @@ static int topk_select_launch(const char* nm, const void* keys, int key_type, in
                        n, k, n_sink, n_local, nseg, h, idx_out, stride);
     return check_launch(nm);
   }
-  if (key_type == SDQ_KEY_F32_MAX)
+  if (key_type == SDQ_KEY_F32_MAX && n - n_sink - n_local <= kRowLdsMax)
+    hipLaunchKernelGGL(topk_row_lds_kernel, dim3(rows), dim3(kTkThreads), 0, stream, fk, n, k,
+                       n_sink, n_local, idx_out, stride);
+  else if (key_type == SDQ_KEY_F32_MAX)
     hipLaunchKernelGGL(topk_row_kernel<SDQ_KEY_F32_MAX>, dim3(rows), dim3(kTkThreads), 0, stream,
                        keys, n, k, n_sink, n_local, idx_out, stride);
   else

@@ -292,7 +292,10 @@ def _topk_ref(keys, k, n_sink, n_local, largest):
 @pytest.mark.parametrize("rows,n,k,ns,nl", [(3, 1, 1, 0, 0), (2, 100, 7, 0, 0), (4, 4096, 64, 0, 0),
                                             (2, 5000, 512, 3, 17), (1, 1000, 2000, 0, 0),
                                             (2, 70001, 512, 0, 0), (8, 1 << 20, 512, 0, 0),
-                                            (2, 200000, 3000, 128, 128), (3, 300, 0, 5, 5)])
+                                            (2, 200000, 3000, 128, 128), (3, 300, 0, 5, 5),
+                                            (8, 32768, 512, 0, 0), (2, 32788, 300, 10, 10),
+                                            (2, 32809, 100, 20, 20), (3, 40000, 2000, 0, 0),
+                                            (2, 16384, 16383, 0, 0), (1, 32768, 32768, 0, 0)])
 def test_topk_f32_bitexact(sdq, rows, n, k, ns, nl):
     _say(f"topk f32 rows={rows} n={n} k={k}")
     g = np.random.default_rng(n + k)
@@ -316,6 +319,16 @@ def test_topk_f32_degenerate_rows(sdq):
     keys[0, 99999] = 7.0
     got = host(sdq.topk_select(dev(keys), 9000, 1, 1))
     assert np.array_equal(got, _topk_ref(keys, 9000, 1, 1, True))
+    # rows held in LDS (at most 32768 competing keys): all tied, -inf pads,
+    # a single distinct key
+    for n2 in (32768, 4096):
+        keys = np.zeros((3, n2), np.float32)
+        keys[1, n2 - 27:] = -np.inf
+        keys[2, :] = 1.5
+        keys[2, n2 // 2] = 9.0
+        for k2 in (1, 512, n2 - 1):
+            got = host(sdq.topk_select(dev(keys), k2, 0, 0))
+            assert np.array_equal(got, _topk_ref(keys, k2, 0, 0, True)), (n2, k2)
 
 
 @pytest.mark.parametrize("rows,n,k,ns,nl", [(8, 1 << 20, 512, 0, 0), (2, 65536 + 128, 64, 64, 64),
