@@ -118,37 +118,44 @@ struct RingDepth {
   static constexpr int D = T == 1 ? 6 : (T == 2 ? 4 : 3);
 };
 
-// All channels of depth T: list slots [a, end).  Full turns of the ring are
-// straight-line code (D accumulations, each followed by the refill of its
-// slot), so the compiler keeps the refills where they are written and its
-// waits stay exact; refills past the end re-read the run's last channel (an
-// L1 hit).  The last partial turn only drains the ring.
-template <int T>
+// The channels of depth T at list slots a, a + S, a + 2S, ... below end (S = 1,
+// or the number of waves sharing a tile, each taking every S-th channel).
+// Full turns of the ring are straight-line code (D accumulations, each
+// followed by the refill of its slot), so the compiler keeps the refills
+// where they are written and its waits stay exact; refills past the end
+// re-read the run's last channel (an L1 hit).  The last partial turn only
+// drains the ring.
+template <int T, int S>
 __device__ __forceinline__ void accum_run(int a, int end, const int* s_j, const float* s_q,
                                           const float* s_qm, const float* s_q2,
                                           const ScanSrc& src, float& C, float (&acc)[kTok]) {
   constexpr int D = RingDepth<T>::D;
   if (a >= end) return;
+  const int last = a + (end - 1 - a) / S * S;        // the last slot this wave takes
   auto fetch = [&](ChanData<T>& d, int x) {
-    x = x < end ? x : end - 1;
+    x = x < last ? x : last;
     load_chan<T>(d, src, __builtin_amdgcn_readfirstlane(s_j[x]));
   };
   ChanData<T> ring[D];
 #pragma unroll
-  for (int k = 0; k < D; ++k) fetch(ring[k], a + k);
-  const int turns = (end - a) / D;
+  for (int k = 0; k < D; ++k) fetch(ring[k], a + k * S);
+  const int cnt = (last - a) / S + 1;
+  const int turns = cnt / D;
   for (int it = 0; it < turns; ++it) {
 #pragma unroll
     for (int k = 0; k < D; ++k) {
-      use_chan<T>(ring[k], s_q[a + k], s_qm[a + k], s_q2[a + k], C, acc);
-      fetch(ring[k], a + k + D);
+      const int x = a + k * S;
+      use_chan<T>(ring[k], s_q[x], s_qm[x], s_q2[x], C, acc);
+      fetch(ring[k], x + D * S);
     }
-    a += D;
+    a += D * S;
   }
-  const int rem = end - a;
+  const int rem = cnt - turns * D;
 #pragma unroll
-  for (int k = 0; k < D; ++k)
-    if (k < rem) use_chan<T>(ring[k], s_q[a + k], s_qm[a + k], s_q2[a + k], C, acc);
+  for (int k = 0; k < D; ++k) {
+    const int x = a + k * S;
+    if (k < rem) use_chan<T>(ring[k], s_q[x], s_qm[x], s_q2[x], C, acc);
+  }
 }
 
 // Plan inputs of the fused kernel (every workgroup derives its head's plan).
@@ -161,7 +168,13 @@ struct PlanIn {
 };
 
 // MODE 0: plan read from depth/qbar; 1: water-filling plan; 2: uniform plan.
-template <int MODE>
+// SPLIT false: each wave scores its own 64 words (2048 tokens) over every
+// active channel.  SPLIT true (short rows, too few words to fill the GPU
+// with one wave each): the workgroup's waves share one 64-word tile, wave v
+// takes every kScanWaves-th channel of each depth run, and the partial sums
+// meet in LDS, so a tile's dependent chain of load turns is kScanWaves times
+// shorter.
+template <int MODE, bool SPLIT>
 __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
     const uint32_t* __restrict__ planes, const uint32_t* __restrict__ meta,
     const uint8_t* __restrict__ depth, const float* __restrict__ qbar, int n, int nb64, int n_cap,
@@ -241,8 +254,9 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
 
   const size_t nw = size_t(nb64) * 2;                            // words scored (n rounded up to 64)
   const size_t nw_cap = size_t(n_cap) / 32;                       // words per plane row
-  const int wd = (blockIdx.x * kScanWaves + wave) * 64 + lane;   // this lane's 32-token word
-  if ((blockIdx.x * kScanWaves + wave) * 64 >= int(nw)) return;   // whole wave past the end
+  const int tile = SPLIT ? int(blockIdx.x) : int(blockIdx.x) * kScanWaves + wave;
+  const int wd = tile * 64 + lane;                                // this lane's 32-token word
+  if (tile * 64 >= int(nw)) return;                               // whole wave past the end
   const bool valid = wd < int(nw);
   const int wdc = valid ? wd : int(nw) - 1;                       // loads stay in bounds
   const int b = wdc >> 1;
@@ -266,10 +280,31 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
   for (int i = 0; i < kTok; ++i) acc[i] = 0.0f;
   const int r0 = __builtin_amdgcn_readfirstlane(s_run[0]), r1 = __builtin_amdgcn_readfirstlane(s_run[1]);
   const int r2 = __builtin_amdgcn_readfirstlane(s_run[2]), r3 = __builtin_amdgcn_readfirstlane(s_run[3]);
-  accum_run<4>(r0, r1, s_j, s_q, s_qm, s_q2, src, C, acc);
-  accum_run<3>(r1, r2, s_j, s_q, s_qm, s_q2, src, C, acc);
-  accum_run<2>(r2, r3, s_j, s_q, s_qm, s_q2, src, C, acc);
-  accum_run<1>(r3, A, s_j, s_q, s_qm, s_q2, src, C, acc);
+  constexpr int S = SPLIT ? kScanWaves : 1;
+  const int v = SPLIT ? wave : 0;
+  accum_run<4, S>(r0 + v, r1, s_j, s_q, s_qm, s_q2, src, C, acc);
+  accum_run<3, S>(r1 + v, r2, s_j, s_q, s_qm, s_q2, src, C, acc);
+  accum_run<2, S>(r2 + v, r3, s_j, s_q, s_qm, s_q2, src, C, acc);
+  accum_run<1, S>(r3 + v, A, s_j, s_q, s_qm, s_q2, src, C, acc);
+  if constexpr (SPLIT) {
+    // waves 1.. hand their partial sums to wave 0, which adds them in wave
+    // order (the staging rows of waves 1.. are free until then)
+    if (wave > 0) {
+      float* part = reinterpret_cast<float*>(s_out[wave]);
+#pragma unroll
+      for (int i = 0; i < kTok; ++i) part[i * 64 + lane] = acc[i];
+      part[kTok * 64 + lane] = C;
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 1; w < kScanWaves; ++w) {
+      const float* part = reinterpret_cast<const float*>(s_out[w]);
+#pragma unroll
+      for (int i = 0; i < kTok; ++i) acc[i] += part[i * 64 + lane];
+      C += part[kTok * 64 + lane];
+    }
+  }
 
   float sv[kTok];
   float m = -INFINITY;
@@ -278,7 +313,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
     const int pos = (i & 15) < 8 ? (i & 15) : (i & 15) - 8;    // acc[i] holds 2^pos x its sum
     sv[i] = __builtin_fmaf(acc[i], __builtin_bit_cast(float, uint32_t(127 - pos) << 23), C);
   }
-  const int wbase = (blockIdx.x * kScanWaves + wave) * 64;       // first word of the wave
+  const int wbase = tile * 64;                                    // first word of the tile
   if ((wbase + 64) * kTok > n) {                                  // the wave holds tokens past n
 #pragma unroll
     for (int i = 0; i < kTok; ++i) sv[i] = wd * kTok + i < n ? sv[i] : -INFINITY;
@@ -312,6 +347,14 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
 
 using namespace sdq;
 
+// Rows too short to give every CU its share of one-wave tiles: the waves of
+// a workgroup share a tile instead (at most 1024 tiles over all KV heads,
+// i.e. 4096 waves, 16 per CU).
+static bool scan_split(int G, int nb64) {
+  const long long tiles = (long long)G * ((2LL * nb64 + 63) / 64);
+  return tiles <= 1024;
+}
+
 static int scan_checks(const char* nm, const uint32_t* planes, const uint32_t* meta, int G,
                        int d, int n, int n_cap, const float* scores) {
   SDQ_REQUIRE(planes && meta && scores, "%s: null pointer", nm);
@@ -332,9 +375,14 @@ extern "C" int fathom_scan(const uint32_t* planes, const uint32_t* meta, const u
   SDQ_REQUIRE(depth && qbar, "fathom_scan: null pointer");
   if (const int rc = scan_checks("fathom_scan", planes, meta, G, d, n, n_cap, scores)) return rc;
   const int nb64 = (n + 63) / 64;
-  dim3 grid(cdiv(size_t(nb64) * 2, kScanWaves * 64), G);
-  hipLaunchKernelGGL(fathom_scan_kernel<0>, grid, dim3(kScanWaves * 64), 0, stream, planes, meta,
-                     depth, qbar, n, nb64, n_cap, scores, block_max, PlanIn{});
+  if (scan_split(G, nb64))
+    hipLaunchKernelGGL((fathom_scan_kernel<0, true>), dim3(cdiv(size_t(nb64) * 2, 64), G),
+                       dim3(kScanWaves * 64), 0, stream, planes, meta, depth, qbar, n, nb64, n_cap,
+                       scores, block_max, PlanIn{});
+  else
+    hipLaunchKernelGGL((fathom_scan_kernel<0, false>), dim3(cdiv(size_t(nb64) * 2, kScanWaves * 64), G),
+                       dim3(kScanWaves * 64), 0, stream, planes, meta, depth, qbar, n, nb64, n_cap,
+                       scores, block_max, PlanIn{});
   return check_launch("fathom_scan");
 }
 
@@ -350,13 +398,21 @@ extern "C" int fathom_plan_scan(const float* q, const float* key_var, int H_grp,
   SDQ_REQUIRE(!uniform || budget <= d, "fathom_plan_scan: n_channels=%d exceeds d=%d", budget, d);
   if (const int rc = scan_checks("fathom_plan_scan", planes, meta, G, d, n, n_cap, scores)) return rc;
   const int nb64 = (n + 63) / 64;
-  dim3 grid(cdiv(size_t(nb64) * 2, kScanWaves * 64), G);
   const PlanIn pin{q, key_var, H_grp, budget, depth, qbar};
-  if (uniform)
-    hipLaunchKernelGGL(fathom_scan_kernel<2>, grid, dim3(kScanWaves * 64), 0, stream, planes, meta,
-                       nullptr, nullptr, n, nb64, n_cap, scores, block_max, pin);
+  const bool split = scan_split(G, nb64);
+  const dim3 grid(cdiv(size_t(nb64) * 2, split ? 64 : kScanWaves * 64), G);
+  const dim3 block(kScanWaves * 64);
+  if (uniform && split)
+    hipLaunchKernelGGL((fathom_scan_kernel<2, true>), grid, block, 0, stream, planes, meta, nullptr,
+                       nullptr, n, nb64, n_cap, scores, block_max, pin);
+  else if (uniform)
+    hipLaunchKernelGGL((fathom_scan_kernel<2, false>), grid, block, 0, stream, planes, meta, nullptr,
+                       nullptr, n, nb64, n_cap, scores, block_max, pin);
+  else if (split)
+    hipLaunchKernelGGL((fathom_scan_kernel<1, true>), grid, block, 0, stream, planes, meta, nullptr,
+                       nullptr, n, nb64, n_cap, scores, block_max, pin);
   else
-    hipLaunchKernelGGL(fathom_scan_kernel<1>, grid, dim3(kScanWaves * 64), 0, stream, planes, meta,
-                       nullptr, nullptr, n, nb64, n_cap, scores, block_max, pin);
+    hipLaunchKernelGGL((fathom_scan_kernel<1, false>), grid, block, 0, stream, planes, meta, nullptr,
+                       nullptr, n, nb64, n_cap, scores, block_max, pin);
   return check_launch("fathom_plan_scan");
 }
