@@ -392,7 +392,7 @@ def main():
         "kernel": "fathom_plan_scan", "bytes_per_launch": scan_bytes,
         "launch_us": round(scan_launch_us, 2),
         "launch_timing": "mean of 64 back-to-back launches (one replayed HIP graph) over the 8 rotating index copies",
-        "trace_avg_us": trace_average(TRACE_FILE, "fathom_scan_kernel<1>"),
+        "trace_avg_us": trace_average(TRACE_FILE, "fathom_scan_kernel<1, false>"),
         "floor_us": round(max(t_hbm, t_valu) * 1e6, 2),
         "frac_of_binding_floor": round(max(t_hbm, t_valu) / scan_s, 4),
         "fixed_cost_us": round(scan_fixed_us, 2),
@@ -962,6 +962,23 @@ def copy_calibration(torch, dev):
     return src.numel() * 4
 
 
+def same_size_reference(torch, dev, reps=20):
+    """Plain streaming kernels of the Hamming scan's size, for its kernel
+    trace: a device copy moving 21 MB (10.5 MB read, 10.5 MB written; the
+    distance kernel moves 16.8 MB of signatures read and 4.2 MB of distances
+    written) and a 16.8 MB read with a row sum.  Their durations are what a kernel of this size takes once
+    launch, ramp and drain are counted."""
+    src = torch.ones(2_621_440, dtype=torch.float32, device=dev)      # 10.5 MB each way
+    dst = torch.empty_like(src)
+    sig = torch.ones(32, 131072, dtype=torch.int32, device=dev)
+    out = torch.empty(32, dtype=torch.int64, device=dev)
+    for _ in range(reps):
+        dst.copy_(src)
+        torch.sum(sig, dim=1, out=out)
+    torch.cuda.synchronize()
+    return {"copy_bytes": src.numel() * 4 * 2, "read_bytes": sig.numel() * 4, "reps": reps}
+
+
 def run_variant(args):
     """--variant hamming|minmax|oasis: only that step, W warm-up + K steps (the
     resident-pool step fills its pool first, untimed, and times K steps), for
@@ -993,6 +1010,8 @@ def run_variant(args):
             "us_per_step": round(e0.elapsed_time(e1) / args.steps * 1e3, 2)}
     if args.copy_calibration:
         line["copy_calibration_bytes"] = copy_calibration(torch, dev)
+        if args.variant == "hamming":
+            line["same_size_reference"] = same_size_reference(torch, dev)
     print(json.dumps(line), flush=True)
 
 

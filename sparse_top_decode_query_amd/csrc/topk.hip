@@ -34,7 +34,8 @@ namespace sdq {
 
 constexpr int kTkThreads = 512;
 constexpr int kTkWaves = kTkThreads / 64;
-constexpr int kFastMinComp = 65536;        // competition length that takes the fast path
+constexpr int kFastMinComp = 32769;        // competition length that takes the fast path
+constexpr int kBmMinComp = 65536;          // ... and the block-max path
 constexpr int kHistBins = 2048;            // top 11 bits of the code
 constexpr int kHistShift = 21;
 constexpr int kCandCap = 8192;             // candidates per row
@@ -82,6 +83,13 @@ __device__ __forceinline__ void block_scan2(int a, int b, int& ea, int& eb, int&
   ea = wa + ia - a;
   eb = wb + ib - b;
   __syncthreads();
+}
+
+// Block-wide exclusive prefix sum of one counter (512 threads).
+__device__ __forceinline__ int block_scan1(int a, int& total, int* s_scan) {
+  int ea, eb, tb;
+  block_scan2(a, 0, ea, eb, total, tb, s_scan);
+  return ea;
 }
 
 // k-th largest of a set of 32-bit codes, for a whole 512-thread workgroup.
@@ -259,22 +267,45 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const void* __rest
   topk_row<KT>(keys, size_t(row) * n, n, k, n_sink, n_local, out + size_t(row) * stride, stride);
 }
 
-// Rows short enough to sit in LDS (float32, at most kRowLdsMax competing
-// keys): the row's order-preserving codes are read from memory once, every
-// load in flight together, and the selection passes and the ordered write
-// then read LDS instead of memory.  Same ordering and output as topk_row.
+// Rows short enough to sit in LDS (float32, at most CAP competing keys): the
+// row's order-preserving codes are read from memory once, every load in
+// flight together, and every later pass reads LDS:
+//  1. codes into LDS and their range;
+//  2. a 4096-bin histogram over the range; the bin b* holding the K-th
+//     largest code;
+//  3. the codes of bin b* compacted into a short list (thread t owns a
+//     contiguous chunk of the row: count, one prefix sum, write);
+//  4. the exact K-th code and its tie count among them;
+//  5. the winners written in index order (count per chunk, one prefix sum,
+//     write).
+// Code i sits at LDS word i + i/32, so both the strided passes (thread t reads
+// codes t, t + 512, ...) and the chunked ones (thread t reads its chunk) are
+// free of bank conflicts or nearly so.  Same ordering and output as topk_row.
+// Two sizes: the large one fills a CU's LDS (one workgroup per CU), the small
+// one lets many short rows share a CU.
 constexpr int kRowLdsMax = 32768;
+constexpr int kRowLdsSmall = 4096;
+constexpr int kRowLdsMin = 1024;     // shorter rows stay on the row path (cache-resident re-reads)
 
+__device__ __forceinline__ int lds_pad(int i) { return i + (i >> 5); }
+
+template <int CAP>
 __global__ __launch_bounds__(kTkThreads) void topk_row_lds_kernel(const float* __restrict__ keys,
                                                                   int n, int k, int n_sink,
                                                                   int n_local,
                                                                   int32_t* __restrict__ out,
                                                                   int stride) {
-  __shared__ uint32_t s_code[kRowLdsMax];
+  constexpr int kBins = 4096;                  // first-pass histogram
+  constexpr int kCand = 2048;                  // codes of the threshold bin kept for the exact pass
+  __shared__ uint32_t s_code[CAP + CAP / 32];
+  __shared__ uint32_t s_bin[kBins];
+  __shared__ uint32_t s_cand[kCand];
   __shared__ uint32_t hist[256];
   __shared__ int s_scan[2 * kTkWaves];
   __shared__ uint32_t s_red[2 * kTkWaves];
-  const int row = blockIdx.x, tid = threadIdx.x;
+  __shared__ uint32_t s_bstar;
+  __shared__ int s_need;
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int32_t* o = out + size_t(row) * stride;
   const int lo = n_sink, hi = n - n_local, m = hi - lo;
   const int K = k < m ? k : m;
@@ -284,70 +315,137 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_lds_kernel(const float* _
     return;
   }
   if (K == 0) return;
+  // 1. codes into LDS (16 unconditional loads per thread in flight; indices
+  //    past the row re-read its last key) and their range
   const float* src = keys + size_t(row) * n + lo;
-  constexpr int LPT = 16;                      // loads per thread issued together
+  constexpr int LPT = 16;
+  uint32_t cmin = 0xFFFFFFFFu, cmax = 0u;
   for (int c0 = 0; c0 < m; c0 += kTkThreads * LPT) {
     float v[LPT];
 #pragma unroll
     for (int e = 0; e < LPT; ++e) {
       const int i = c0 + e * kTkThreads + tid;
-      v[e] = i < m ? src[i] : 0.0f;
+      v[e] = src[i < m ? i : m - 1];
     }
 #pragma unroll
     for (int e = 0; e < LPT; ++e) {
       const int i = c0 + e * kTkThreads + tid;
-      if (i < m) s_code[i] = f32_order_key(v[e]);
+      const uint32_t u = f32_order_key(v[e]);
+      if (i < m) s_code[lds_pad(i)] = u;
+      cmin = u < cmin ? u : cmin;              // the re-read last key is in range anyway
+      cmax = u > cmax ? u : cmax;
+    }
+  }
+  for (int i = tid; i < kBins; i += kTkThreads) s_bin[i] = 0;
+  cmin = wave_minmax_u32<false>(cmin);
+  cmax = wave_minmax_u32<true>(cmax);
+  if (lane == 0) {
+    s_red[wave] = cmin;
+    s_red[kTkWaves + wave] = cmax;
+  }
+  __syncthreads();
+  cmin = 0xFFFFFFFFu;
+  cmax = 0u;
+#pragma unroll
+  for (int w = 0; w < kTkWaves; ++w) {
+    cmin = s_red[w] < cmin ? s_red[w] : cmin;
+    cmax = s_red[kTkWaves + w] > cmax ? s_red[kTkWaves + w] : cmax;
+  }
+  // 2. histogram of the codes in kBins bins of width 2^sh over [cmin, cmax],
+  //    and the bin b* holding the K-th largest
+  const int wbits = 32 - __clz(cmax - cmin);
+  const int sh = wbits > 12 ? wbits - 12 : 0;
+#pragma unroll 8
+  for (int i = tid; i < m; i += kTkThreads) atomicAdd(&s_bin[(s_code[lds_pad(i)] - cmin) >> sh], 1u);
+  __syncthreads();
+  {
+    constexpr int BT = kBins / kTkThreads;            // bins BT*t .. BT*t+BT-1
+    int cnt[BT], lsum = 0;
+#pragma unroll
+    for (int e = 0; e < BT; ++e) {
+      cnt[e] = int(s_bin[BT * tid + e]);
+      lsum += cnt[e];
+    }
+    int tot;
+    const int before = block_scan1(lsum, tot, s_scan);
+    int above = tot - before - lsum;                  // codes in higher threads' bins
+#pragma unroll
+    for (int e = BT - 1; e >= 0; --e) {
+      if (above < K && above + cnt[e] >= K) {
+        s_bstar = uint32_t(BT * tid + e);
+        s_need = K - above;
+      }
+      above += cnt[e];
     }
   }
   __syncthreads();
-  const KthResult kr = select_kth(
-      m, K,
-      [&](int i, uint32_t* u) {
-        *u = s_code[i];
-        return true;
-      },
-      hist, s_red);
+  const uint32_t bstar = s_bstar;
+  int need = s_need;
+  // 3. the codes of bin b* into a short list, chunk by chunk in order
+  const int W = (m + kTkThreads - 1) / kTkThreads;    // codes per thread chunk
+  const int j0 = tid * W, j1 = j0 + W < m ? j0 + W : m;
+  int mine = 0;
+#pragma unroll 8
+  for (int j = j0; j < j1; ++j) mine += ((s_code[lds_pad(j)] - cmin) >> sh) == bstar;
+  int ncand;
+  int slot = block_scan1(mine, ncand, s_scan);
+  if (ncand <= kCand && mine) {
+#pragma unroll 8
+    for (int j = j0; j < j1; ++j) {
+      const uint32_t u = s_code[lds_pad(j)];
+      if (((u - cmin) >> sh) == bstar) s_cand[slot++] = u;
+    }
+  }
+  __syncthreads();
+  // 4. the exact K-th code and how many of its ties to keep (all codes above
+  //    bin b* are in the top K already)
+  KthResult kr;
+  if (ncand <= kCand) {
+    kr = select_kth(
+        ncand, need,
+        [&](int i, uint32_t* u) {
+          *u = s_cand[i];
+          return true;
+        },
+        hist, s_red);
+  } else {                                            // a crowded bin: every code
+    kr = select_kth(
+        m, K,
+        [&](int i, uint32_t* u) {
+          *u = s_code[lds_pad(i)];
+          return true;
+        },
+        hist, s_red);
+  }
   const uint32_t T = kr.T;
-  const int need = kr.need;
-  constexpr int IPT = 8;
-  int out_pos = n_sink, eq_seen = 0;
-  for (int c0 = 0; c0 < m; c0 += kTkThreads * IPT) {
-    const int i0 = c0 + tid * IPT;
-    uint32_t u[IPT];
-    int gt = 0, eq = 0;
-#pragma unroll
-    for (int e = 0; e < IPT; ++e) {
-      const int i = i0 + e;
-      u[e] = i < m ? s_code[i] : 0u;
-      if (i < m) {
-        gt += u[e] > T;
-        eq += u[e] == T;
+  need = kr.need;
+  // 5. winners in index order: every code above T, and the first `need`
+  //    codes equal to T
+  int gt = 0, eq = 0;
+#pragma unroll 8
+  for (int j = j0; j < j1; ++j) {
+    const uint32_t u = s_code[lds_pad(j)];
+    gt += u > T;
+    eq += u == T;
+  }
+  int egt, eeq, tgt, teq;
+  block_scan2(gt, eq, egt, eeq, tgt, teq, s_scan);
+  int pos = n_sink + egt + (eeq < need ? eeq : need);
+  int my_eq = eeq;
+  const int end = n_sink + K;
+#pragma unroll 8
+  for (int j = j0; j < j1; ++j) {
+    const uint32_t u = s_code[lds_pad(j)];
+    if (u > T) {
+      if (pos < end) o[pos] = lo + j;
+      ++pos;
+    } else if (u == T) {
+      if (my_eq < need) {
+        if (pos < end) o[pos] = lo + j;
+        ++pos;
       }
+      ++my_eq;
     }
-    int egt, eeq, tgt, teq;
-    block_scan2(gt, eq, egt, eeq, tgt, teq, s_scan);
-    const int eq_left = need - eq_seen > 0 ? need - eq_seen : 0;
-    int pos = out_pos + egt + (eeq < eq_left ? eeq : eq_left);
-    int my_eq = eeq;
-    const int end = n_sink + K;
-#pragma unroll
-    for (int e = 0; e < IPT; ++e) {
-      const int i = i0 + e;
-      if (i < m) {
-        if (u[e] > T) {
-          if (pos < end) o[pos] = lo + i;
-          ++pos;
-        } else if (u[e] == T) {
-          if (my_eq < eq_left) {
-            if (pos < end) o[pos] = lo + i;
-            ++pos;
-          }
-          ++my_eq;
-        }
-      }
-    }
-    out_pos += tgt + (teq < eq_left ? teq : eq_left);
-    eq_seen += teq;
   }
 }
 
@@ -402,10 +500,18 @@ __global__ __launch_bounds__(256) void topk_bin_kernel(void* ws, int K) {
     c[e] = int(gh[8 * tid + e]);
     tot += c[e];
   }
-  s_part[tid] = tot;
+  // codes in bins of higher threads: the total minus this thread's inclusive
+  // prefix (wave scans, then the four wave totals through LDS)
+  const int inc = wave_incl_scan(tot);
+  if ((tid & 63) == 63) s_part[tid >> 6] = inc;
   __syncthreads();
-  int above = 0;                       // codes in bins of higher threads
-  for (int t = tid + 1; t < 256; ++t) above += s_part[t];
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    before += w < (tid >> 6) ? s_part[w] : 0;
+    all += s_part[w];
+  }
+  int above = all - (before + inc);
   int S_next = above;                  // codes in bins above the current one
 #pragma unroll
   for (int e = 7; e >= 0; --e) {
@@ -993,12 +1099,6 @@ __device__ __forceinline__ float f32_from_order_key(uint32_t c) {
   return __uint_as_float((c & 0x80000000u) ? (c & 0x7FFFFFFFu) : ~c);
 }
 
-// Block-wide exclusive prefix sum of one counter (512 threads).
-__device__ __forceinline__ int block_scan1(int a, int& total, int* s_scan) {
-  int ea, eb, tb;
-  block_scan2(a, 0, ea, eb, total, tb, s_scan);
-  return ea;
-}
 
 __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __restrict__ keys,
                                                              const float* __restrict__ bm, int n,
@@ -1269,7 +1369,7 @@ static bool use_fast(int n, int n_sink, int n_local, int k, int key_type) {
 
 static bool use_block_max(int n, int n_sink, int n_local, int k, int key_type) {
   const int m = n - n_sink - n_local;
-  return key_type == SDQ_KEY_F32_MAX && m >= kFastMinComp && n % 64 == 0 && n_sink % 64 == 0 &&
+  return key_type == SDQ_KEY_F32_MAX && m >= kBmMinComp && n % 64 == 0 && n_sink % 64 == 0 &&
          n_local % 64 == 0 && n / 64 <= kBmMaxBlocks && k < m && k <= m / 64;
 }
 
@@ -1359,9 +1459,13 @@ static int topk_select_launch(const char* nm, const void* keys, int key_type, in
                        n, k, n_sink, n_local, nseg, h, idx_out, stride);
     return check_launch(nm);
   }
-  if (key_type == SDQ_KEY_F32_MAX && n - n_sink - n_local <= kRowLdsMax)
-    hipLaunchKernelGGL(topk_row_lds_kernel, dim3(rows), dim3(kTkThreads), 0, stream, fk, n, k,
-                       n_sink, n_local, idx_out, stride);
+  const int m_comp = n - n_sink - n_local;
+  if (key_type == SDQ_KEY_F32_MAX && m_comp > kRowLdsMin && m_comp <= kRowLdsSmall)
+    hipLaunchKernelGGL(topk_row_lds_kernel<kRowLdsSmall>, dim3(rows), dim3(kTkThreads), 0, stream,
+                       fk, n, k, n_sink, n_local, idx_out, stride);
+  else if (key_type == SDQ_KEY_F32_MAX && m_comp > kRowLdsMin && m_comp <= kRowLdsMax)
+    hipLaunchKernelGGL(topk_row_lds_kernel<kRowLdsMax>, dim3(rows), dim3(kTkThreads), 0, stream,
+                       fk, n, k, n_sink, n_local, idx_out, stride);
   else if (key_type == SDQ_KEY_F32_MAX)
     hipLaunchKernelGGL(topk_row_kernel<SDQ_KEY_F32_MAX>, dim3(rows), dim3(kTkThreads), 0, stream,
                        keys, n, k, n_sink, n_local, idx_out, stride);
