@@ -606,6 +606,16 @@ def run_extras(torch, np, lib, bytemodel, synth, dev, case, K4, V4, q, var, q3, 
     ex["quality_1M"] = quality.evaluate(K4[0], V4[0], q, var, index, case["needle_pos"], k)
     log(f"extras: plan quality in {time.time() - t0:.1f} s")
     torch.cuda.empty_cache()
+    # the 32k-token layer whose lifted keys separate the plans: a sweep of budgets
+    # and uniform plans and the equal-error bits against the uniform 136-bit plan
+    t0 = time.time()
+    qa = quality.run(2, layer="aligned", sweep=True)
+    keep = ("plan_bits", "scan_bytes", "mass_mean", "rel_err_mean", "exact_topk_recall", "needle_recall")
+    ex["quality_aligned_32k"] = {
+        "equal_error": qa["equal_error"], "exact_topk": qa["exact_topk"],
+        "plans": {name: {f: row[f] for f in keep} for name, row in qa["plans"].items()}}
+    log(f"extras: aligned-layer sweep in {time.time() - t0:.1f} s")
+    torch.cuda.empty_cache()
 
     us_step, us_scan, info = variant_hamming(torch, np, lib, bytemodel, synth, dev, timeit_graph)
     if not no_cpu:

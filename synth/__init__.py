@@ -53,6 +53,12 @@ SIGMA_LO, SIGMA_HI = 0.05, 4.0
 # stream tags (arbitrary distinct integers)
 _T_SIGMA, _T_SIGMA_V, _T_Q, _T_BOOST, _T_K, _T_V, _T_NEEDLE = 11, 12, 13, 14, 15, 16, 17
 _T_SIG, _T_QSIG, _T_PLANT_POS, _T_PLANT_MASK = 21, 22, 23, 24
+_T_ALIGN_POS, _T_ALIGN_T = 31, 32
+
+# Layer "aligned": keys per KV head lifted along the group query, and the range
+# of the lift in units of the bulk score's standard deviation.
+ALIGNED_KEYS = 512
+ALIGNED_LIFT = (3.0, 6.0)
 
 
 def seed_of(cfg: int) -> int:
@@ -112,7 +118,8 @@ def _fill_heads(out: np.ndarray, seed: int, tag: int, heads, sigmas) -> None:
 # --------------------------------------------------------------------------
 # Bit-plane (Fathom) workloads: configs 1-3
 # --------------------------------------------------------------------------
-def fathom_case(cfg: int, n: int | None = None, heads=None, with_values: bool = True) -> dict:
+def fathom_case(cfg: int, n: int | None = None, heads=None, with_values: bool = True,
+                layer: str = "needles") -> dict:
     """One decode layer for the bit-plane index.
 
     Keys: bf16 N(0, sigma_j^2) per (KV head, channel), sigma log-uniform on
@@ -125,11 +132,22 @@ def fathom_case(cfg: int, n: int | None = None, heads=None, with_values: bool = 
     the typical key norm.  Values: bf16 N(0,1) (config 1) or N(0, sigma'_j^2)
     with sigma' drawn independently from the same law (configs 2-3).
 
+    ``layer="aligned"`` plants no needles.  Instead ALIGNED_KEYS = 512
+    distinct positions per KV head (or n, if fewer) keep their normal draw k
+    and add t * tau * qsum / |qsum|^2, with t uniform on [3, 6] per key and
+    tau = sqrt(sum_j qsum_j^2 sigma_j^2) the standard deviation of qsum . k
+    under the key law.  Their group score is the bulk's plus t standard
+    deviations, and their norm stays near the bulk's, so which of them a scan
+    ranks into the top k depends on how precisely it reads: a layer on which
+    read plans of different depth give different attention mass, error and
+    recall.  ``needle_pos`` then holds these positions.
+
     ``n`` overrides the token count (same per-chunk draws, so a shorter case
     is a prefix of the long one except for needle positions); ``heads``
     restricts the KV heads that are materialised (their bytes are identical to
     those in the full case).
     """
+    assert layer in ("needles", "aligned")
     c = CONFIGS[cfg]
     assert c["kind"] == "fathom"
     seed = seed_of(cfg)
@@ -151,8 +169,19 @@ def fathom_case(cfg: int, n: int | None = None, heads=None, with_values: bool = 
     K = np.empty((len(heads), n, D), np.uint16)
     _fill_heads(K, seed, _T_K, heads, sigma)
 
-    needle_pos = np.zeros((len(heads), c["needles"]), np.int64)
-    if c["needles"]:
+    if layer == "aligned":
+        m = min(ALIGNED_KEYS, n)
+        needle_pos = np.zeros((len(heads), m), np.int64)
+        for hi, g in enumerate(heads):
+            pos = np.sort(rng(seed, _T_ALIGN_POS, g, n).choice(n, size=m, replace=False))
+            t = rng(seed, _T_ALIGN_T, g, n).uniform(*ALIGNED_LIFT, size=m)
+            qsum = q[g * Hgrp:(g + 1) * Hgrp].astype(np.float64).sum(axis=0)
+            tau = math.sqrt(float((qsum ** 2 * sigma[g].astype(np.float64) ** 2).sum()))
+            lift = (t * tau / float(qsum @ qsum))[:, None] * qsum[None, :]
+            K[hi, pos] = f32_to_bf16_bits((bf16_bits_to_f32(K[hi, pos]) + lift).astype(np.float32))
+            needle_pos[hi] = pos
+    elif c["needles"]:
+        needle_pos = np.zeros((len(heads), c["needles"]), np.int64)
         for hi, g in enumerate(heads):
             pos = np.sort(rng(seed, _T_NEEDLE, g, n).choice(n, size=c["needles"], replace=False))
             qsum = q[g * Hgrp:(g + 1) * Hgrp].astype(np.float64).sum(axis=0)
@@ -160,9 +189,11 @@ def fathom_case(cfg: int, n: int | None = None, heads=None, with_values: bool = 
             vec = (norm * qsum / np.linalg.norm(qsum)).astype(np.float32)
             K[hi, pos] = f32_to_bf16_bits(vec[None, :])[0]
             needle_pos[hi] = pos
+    else:
+        needle_pos = np.zeros((len(heads), 0), np.int64)
 
     out = dict(cfg=cfg, G=G, Hgrp=Hgrp, n=n, d=D, heads=heads, sigma=sigma, var=var,
-               q=q, K=K, needle_pos=needle_pos, budget=c["budget"], k=c["k"])
+               q=q, K=K, needle_pos=needle_pos, budget=c["budget"], k=c["k"], layer=layer)
     if with_values:
         if c["v_sigma"] == "unit":
             vs = None
