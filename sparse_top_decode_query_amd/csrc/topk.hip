@@ -57,7 +57,10 @@ __device__ __forceinline__ uint32_t load_code(const void* __restrict__ keys, siz
   return 255u - reinterpret_cast<const uint8_t*>(keys)[i];
 }
 
-// Block-wide exclusive prefix sums of two counters (512 threads).
+// Block-wide exclusive prefix sums of two counters (512 threads).  With
+// kTail = false the closing barrier is left out: the caller must pass a
+// barrier (or use another s_scan buffer) before s_scan is written again.
+template <bool kTail = true>
 __device__ __forceinline__ void block_scan2(int a, int b, int& ea, int& eb, int& ta, int& tb,
                                             int* s_scan) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -82,13 +85,14 @@ __device__ __forceinline__ void block_scan2(int a, int b, int& ea, int& eb, int&
   }
   ea = wa + ia - a;
   eb = wb + ib - b;
-  __syncthreads();
+  if (kTail) __syncthreads();
 }
 
 // Block-wide exclusive prefix sum of one counter (512 threads).
+template <bool kTail = true>
 __device__ __forceinline__ int block_scan1(int a, int& total, int* s_scan) {
   int ea, eb, tb;
-  block_scan2(a, 0, ea, eb, total, tb, s_scan);
+  block_scan2<kTail>(a, 0, ea, eb, total, tb, s_scan);
   return ea;
 }
 
@@ -99,10 +103,60 @@ __device__ __forceinline__ int block_scan1(int a, int& total, int* s_scan) {
 // clustered codes do not pile onto one LDS counter), then narrows the range
 // to the bin holding the k-th code.  Returns the code T and how many of the
 // codes equal to T belong to the top k (`need`).
+//
+// One barrier per pass: the passes rotate over three histograms (kKthHist
+// words of LDS), a pass clears the one two passes ahead after its barrier,
+// and every wave finds the k-th bin by itself (four bins a lane and a wave
+// prefix sum), so no result travels through LDS.  Histograms 0 and 1 must be
+// zero on entry to select_kth_in (select_kth clears them); the function ends
+// with a barrier, so hist and s_red are free again on return.
+constexpr int kKthHist = 3 * 256;
+
 struct KthResult {
   uint32_t T;
   int need;
 };
+
+template <typename Fetch>
+__device__ KthResult select_kth_in(int count, int K, Fetch fetch, uint32_t* hist, uint32_t lo,
+                                   uint32_t hi) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  int need = K;
+  for (int p = 0; lo < hi; ++p) {
+    const uint32_t width = hi - lo;
+    const int bits = 32 - __clz(width);                 // width < 2^bits
+    const int sh = bits > 8 ? bits - 8 : 0;              // (width >> sh) < 256
+    uint32_t* h = hist + 256 * (p % 3);
+    for (int i = tid; i < count; i += kTkThreads) {
+      uint32_t u;
+      if (fetch(i, &u) && u >= lo && u <= hi) atomicAdd(&h[(u - lo) >> sh], 1u);
+    }
+    __syncthreads();
+    // the histogram of pass p + 2 was last read before this barrier
+    if (tid < 256) hist[256 * ((p + 2) % 3) + tid] = 0;
+    const uint4 c = *reinterpret_cast<const uint4*>(h + 4 * lane);
+    const int lsum = int(c.x + c.y + c.z + c.w);
+    const int inc = wave_incl_scan(lsum);
+    const int above = wave_last(inc) - inc;             // counts in higher lanes' bins
+    const int S3 = above + int(c.w), S2 = S3 + int(c.z), S1 = S2 + int(c.y);
+    // the one lane whose bins take the count from below `need` to `need` or more
+    const uint64_t hit = __ballot(above < need && above + lsum >= need);
+    const int L = __ffsll((unsigned long long)hit) - 1;
+    int d, rest;
+    if (S3 >= need) { d = 3; rest = need - above; }
+    else if (S2 >= need) { d = 2; rest = need - S3; }
+    else if (S1 >= need) { d = 1; rest = need - S2; }
+    else { d = 0; rest = need - S1; }
+    const uint32_t bin = uint32_t(4 * L + __builtin_amdgcn_readlane(d, L));
+    need = __builtin_amdgcn_readlane(rest, L);
+    const uint32_t nlo = lo + (bin << sh);
+    const uint32_t span = (sh >= 32) ? 0xFFFFFFFFu : ((1u << sh) - 1u);
+    hi = (hi - nlo) > span ? nlo + span : hi;
+    lo = nlo;
+  }
+  __syncthreads();
+  return KthResult{lo, need};
+}
 
 template <typename Fetch>
 __device__ KthResult select_kth(int count, int K, Fetch fetch, uint32_t* hist, uint32_t* s_red) {
@@ -122,6 +176,7 @@ __device__ KthResult select_kth(int count, int K, Fetch fetch, uint32_t* hist, u
     s_red[wave] = mn;
     s_red[kTkWaves + wave] = mx;
   }
+  for (int i = tid; i < 2 * 256; i += kTkThreads) hist[i] = 0;
   __syncthreads();
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
@@ -129,41 +184,7 @@ __device__ KthResult select_kth(int count, int K, Fetch fetch, uint32_t* hist, u
     lo = s_red[w] < lo ? s_red[w] : lo;
     hi = s_red[kTkWaves + w] > hi ? s_red[kTkWaves + w] : hi;
   }
-  __syncthreads();
-  int need = K;
-  while (lo < hi) {
-    const uint32_t width = hi - lo;
-    const int bits = 32 - __clz(width);                 // width < 2^bits
-    const int sh = bits > 8 ? bits - 8 : 0;              // (width >> sh) < 256
-    if (tid < 256) hist[tid] = 0;
-    __syncthreads();
-    for (int i = tid; i < count; i += kTkThreads) {
-      uint32_t u;
-      if (fetch(i, &u) && u >= lo && u <= hi) atomicAdd(&hist[(u - lo) >> sh], 1u);
-    }
-    __syncthreads();
-    if (tid < 64) {
-      const int l = tid;
-      const int c0 = hist[4 * l], c1 = hist[4 * l + 1], c2 = hist[4 * l + 2], c3 = hist[4 * l + 3];
-      const int lsum = c0 + c1 + c2 + c3;
-      const int inc = wave_incl_scan(lsum);
-      const int above = wave_last(inc) - inc;           // counts in higher bins
-      const int S3 = above + c3, S2 = S3 + c2, S1 = S2 + c1, S0 = S1 + c0;
-      if (S3 >= need && above < need) { s_red[0] = 4 * l + 3; s_red[1] = need - above; }
-      if (S2 >= need && S3 < need) { s_red[0] = 4 * l + 2; s_red[1] = need - S3; }
-      if (S1 >= need && S2 < need) { s_red[0] = 4 * l + 1; s_red[1] = need - S2; }
-      if (S0 >= need && S1 < need) { s_red[0] = 4 * l; s_red[1] = need - S1; }
-    }
-    __syncthreads();
-    const uint32_t d = s_red[0];
-    need = int(s_red[1]);
-    __syncthreads();
-    const uint32_t nlo = lo + (d << sh);
-    const uint32_t span = (sh >= 32) ? 0xFFFFFFFFu : ((1u << sh) - 1u);
-    hi = (hi - nlo) > span ? nlo + span : hi;
-    lo = nlo;
-  }
-  return KthResult{lo, need};
+  return select_kth_in(count, K, fetch, hist, lo, hi);
 }
 
 // Reserves one slot per lane with pred set, one LDS atomic per wave.  The
@@ -193,8 +214,8 @@ __device__ __forceinline__ void write_fixed(int32_t* o, int n, int n_sink, int n
 template <int KT>
 __device__ void topk_row(const void* __restrict__ keys, size_t base, int n, int k, int n_sink,
                          int n_local, int32_t* __restrict__ o, int stride) {
-  __shared__ uint32_t hist[256];
-  __shared__ int s_scan[2 * kTkWaves];
+  __shared__ __align__(16) uint32_t hist[kKthHist];
+  __shared__ int s_scan[4 * kTkWaves];    // two buffers: the chunk scans alternate
   const int tid = threadIdx.x;
   const int lo = n_sink, hi = n - n_local, m = hi - lo;
   const int K = k < m ? k : m;
@@ -232,7 +253,8 @@ __device__ void topk_row(const void* __restrict__ keys, size_t base, int n, int 
       }
     }
     int egt, eeq, tgt, teq;
-    block_scan2(gt, eq, egt, eeq, tgt, teq, s_scan);
+    block_scan2<false>(gt, eq, egt, eeq, tgt, teq,
+                       s_scan + 2 * kTkWaves * (((c0 - lo) / (kTkThreads * IPT)) & 1));
     const int eq_left = need - eq_seen > 0 ? need - eq_seen : 0;
     int pos = out_pos + egt + (eeq < eq_left ? eeq : eq_left);
     int my_eq = eeq;
@@ -298,9 +320,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_lds_kernel(const float* _
   constexpr int kBins = 4096;                  // first-pass histogram
   constexpr int kCand = 2048;                  // codes of the threshold bin kept for the exact pass
   __shared__ uint32_t s_code[CAP + CAP / 32];
-  __shared__ uint32_t s_bin[kBins];
+  __shared__ __align__(16) uint32_t s_bin[kBins];
   __shared__ uint32_t s_cand[kCand];
-  __shared__ uint32_t hist[256];
+  __shared__ __align__(16) uint32_t hist[kKthHist];
   __shared__ int s_scan[2 * kTkWaves];
   __shared__ uint32_t s_red[2 * kTkWaves];
   __shared__ uint32_t s_bstar;
@@ -367,7 +389,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_lds_kernel(const float* _
       lsum += cnt[e];
     }
     int tot;
-    const int before = block_scan1(lsum, tot, s_scan);
+    const int before = block_scan1<false>(lsum, tot, s_scan);   // a barrier follows
     int above = tot - before - lsum;                  // codes in higher threads' bins
 #pragma unroll
     for (int e = BT - 1; e >= 0; --e) {
@@ -388,7 +410,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_lds_kernel(const float* _
 #pragma unroll 8
   for (int j = j0; j < j1; ++j) mine += ((s_code[lds_pad(j)] - cmin) >> sh) == bstar;
   int ncand;
-  int slot = block_scan1(mine, ncand, s_scan);
+  int slot = block_scan1<false>(mine, ncand, s_scan);   // a barrier follows
   if (ncand <= kCand && mine) {
 #pragma unroll 8
     for (int j = j0; j < j1; ++j) {
@@ -429,7 +451,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_lds_kernel(const float* _
     eq += u == T;
   }
   int egt, eeq, tgt, teq;
-  block_scan2(gt, eq, egt, eeq, tgt, teq, s_scan);
+  block_scan2<false>(gt, eq, egt, eeq, tgt, teq, s_scan);   // last use of s_scan
   int pos = n_sink + egt + (eeq < need ? eeq : need);
   int my_eq = eeq;
   const int end = n_sink + K;
@@ -562,7 +584,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_final_kernel(const float* __r
                                                                 int32_t* __restrict__ out,
                                                                 int stride) {
   __shared__ uint64_t ck[kCandCap];       // composite keys (u << 32) | ~index
-  __shared__ uint32_t hist[256];
+  __shared__ __align__(16) uint32_t hist[kKthHist];
   __shared__ int sh_cnt;
   const int row = blockIdx.x, tid = threadIdx.x;
   int32_t* o = out + size_t(row) * stride;
@@ -1104,14 +1126,14 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __rest
                                                              const float* __restrict__ bm, int n,
                                                              int nb, int k, int n_sink, int n_local,
                                                              int32_t* __restrict__ out, int stride) {
-  __shared__ uint32_t sbin[kBmBins];
+  __shared__ __align__(16) uint32_t sbin[kBmBins];
   __shared__ int cb[kBmCandBlocks];       // candidate block numbers, ascending
   __shared__ int s_cnt[640];              // kept keys per block of a chunk, then offsets
   __shared__ float ckey[kBmCap];
   __shared__ int cidx[kBmCap];
-  __shared__ uint32_t hist[256];
+  __shared__ __align__(16) uint32_t hist[kKthHist];
   __shared__ uint32_t s_red[2 * kTkWaves];
-  __shared__ int s_scan[2 * kTkWaves];
+  __shared__ int s_scan[4 * kTkWaves];    // two buffers: scans alternate
   __shared__ uint32_t s_thr;
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int32_t* o = out + size_t(row) * stride;
@@ -1182,7 +1204,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __rest
       lsum += cnt[e];
     }
     int tot;
-    const int before = block_scan1(lsum, tot, s_scan);
+    const int before = block_scan1<false>(lsum, tot, s_scan);   // a barrier follows
     int above = tot - before - lsum;                     // maxima in higher threads' bins
 #pragma unroll
     for (int e = BT - 1; e >= 0; --e) {
@@ -1197,7 +1219,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __rest
 #pragma unroll
   for (int u = 0; u < kBmPer; ++u) flags |= uint32_t(mx[u] >= thr) << u;   // -inf never passes
   int ncb;
-  const int cpos = block_scan1(__popc(flags), ncb, s_scan);
+  const int cpos = block_scan1<false>(__popc(flags), ncb, s_scan);   // a barrier follows
   if (ncb > kBmCandBlocks) {
     topk_row<SDQ_KEY_F32_MAX>(keys, base, n, k, n_sink, n_local, o, stride);
     return;
@@ -1259,7 +1281,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __rest
         sum += cnt[e];
       }
       int tot;
-      int off = nc + block_scan1(sum, tot, s_scan);
+      int off = nc + block_scan1<false>(sum, tot, s_scan);           // a barrier follows
 #pragma unroll
       for (int e = 0; e < PT; ++e) {
         const int i = tid * PT + e;
@@ -1332,7 +1354,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __rest
       }
     }
     int egt, eeq, tgt, teq;
-    block_scan2(gt, eq, egt, eeq, tgt, teq, s_scan);
+    block_scan2<false>(gt, eq, egt, eeq, tgt, teq,
+                       s_scan + 2 * kTkWaves * ((c0 / (kTkThreads * IPT)) & 1));
     const int eq_left = kr.need - eq_seen > 0 ? kr.need - eq_seen : 0;
     int pos = out_pos + egt + (eeq < eq_left ? eeq : eq_left);
     int my_eq = eeq;
