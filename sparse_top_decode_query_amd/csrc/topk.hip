@@ -11,8 +11,12 @@
 //    pass, LDS histogram) finds the k-th largest code T and how many of the
 //    codes equal to T to keep; a final pass walks the row in index order and
 //    compacts the winners with block-wide prefix sums, so the output comes out
-//    ascending with no sort.  Used for short float32 rows and as the fallback
-//    of the fast and block-max paths.
+//    ascending with no sort.  Used for float32 rows of at most 1024 keys and
+//    as the fallback of the other paths.
+//  * register row path (one workgroup per row, 1025..32768 float32 keys):
+//    the row is read once into registers, in an order where wave ballots give
+//    index order, and the histogram, candidate and winner passes work on the
+//    registers (see topk_row_reg_kernel).
 //  * uint8 paths: one 256-bin histogram settles the select in a single pass
 //    (one workgroup per row), or, for long rows, per-segment histograms in
 //    the workspace let one workgroup per segment place its own winners.
@@ -289,42 +293,58 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_kernel(const void* __rest
   topk_row<KT>(keys, size_t(row) * n, n, k, n_sink, n_local, out + size_t(row) * stride, stride);
 }
 
-// Rows short enough to sit in LDS (float32, at most CAP competing keys): the
-// row's order-preserving codes are read from memory once, every load in
-// flight together, and every later pass reads LDS:
-//  1. codes into LDS and their range;
-//  2. a 4096-bin histogram over the range; the bin b* holding the K-th
+// Rows of at most CAP competing float32 keys are read from memory once, into
+// registers, and every later pass works on them.  Wave w holds the 64 PER
+// consecutive keys from 64 PER w on, lane l the keys 64 PER w + 64 e + l for
+// e < PER: a wave's loads are contiguous, and (wave, e, lane) is index order,
+// so wave ballots give in-order positions without an LDS copy of the row:
+//  1. order-preserving codes into registers (every load in flight together)
+//     and their range;
+//  2. a 4096-bin LDS histogram over the range; the bin b* holding the K-th
 //     largest code;
-//  3. the codes of bin b* compacted into a short list (thread t owns a
-//     contiguous chunk of the row: count, one prefix sum, write);
-//  4. the exact K-th code and its tie count among them;
-//  5. the winners written in index order (count per chunk, one prefix sum,
-//     write).
-// Code i sits at LDS word i + i/32, so both the strided passes (thread t reads
-// codes t, t + 512, ...) and the chunked ones (thread t reads its chunk) are
-// free of bank conflicts or nearly so.  Same ordering and output as topk_row.
-// Two sizes: the large one fills a CU's LDS (one workgroup per CU), the small
-// one lets many short rows share a CU.
-constexpr int kRowLdsMax = 32768;
-constexpr int kRowLdsSmall = 4096;
-constexpr int kRowLdsMin = 1024;     // shorter rows stay on the row path (cache-resident re-reads)
+//  3. the codes of bin b* compacted into a short LDS list in index order
+//     (per-wave ballot counts, one barrier for the wave offsets);
+//  4. the exact K-th code T and how many of its ties to keep, among them;
+//  5. the winners written in index order: the ballots of "above T" and
+//     "equal to T" for every (wave, e) go to two LDS bitmaps (lane e of the
+//     wave collects word e), then thread t takes bitmap word t, one prefix sum
+//     over the words places its winners, and the first `need` ties in index
+//     order are kept.
+// Slots past the row end (the last PER*512 - m in index order) hold copies of
+// the row's last key, so no pass needs a validity mask: the histogram and the
+// candidate count take the copies back out, and coming last in index order
+// they never take an output position.  A bin b* holding more than kCand codes
+// (heavily tied rows) sends the row to the row path.  Same ordering and output
+// as topk_row.  One size per power of two from 2048 to 32768 keys (4 to 64 a
+// lane), so that no row pays for more than twice its own loads.
+constexpr int kRowRegMin = 1024;     // shorter rows stay on the row path (cache-resident re-reads)
+constexpr int kRowRegMax = 32768;
 
-__device__ __forceinline__ int lds_pad(int i) { return i + (i >> 5); }
+// Lanes below this one with their bit set in a wave mask.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return int(__builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32),
+                                       __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u)));
+}
 
 template <int CAP>
-__global__ __launch_bounds__(kTkThreads) void topk_row_lds_kernel(const float* __restrict__ keys,
+__global__ __launch_bounds__(kTkThreads) void topk_row_reg_kernel(const float* __restrict__ keys,
                                                                   int n, int k, int n_sink,
                                                                   int n_local,
                                                                   int32_t* __restrict__ out,
                                                                   int stride) {
+  constexpr int PER = CAP / kTkThreads;        // keys a lane
+  constexpr int kWords = CAP / 64;             // bitmap words, one per (wave, e)
   constexpr int kBins = 4096;                  // first-pass histogram
   constexpr int kCand = 2048;                  // codes of the threshold bin kept for the exact pass
-  __shared__ uint32_t s_code[CAP + CAP / 32];
-  __shared__ __align__(16) uint32_t s_bin[kBins];
+  static_assert(PER <= 64 && kWords <= kTkThreads, "one bitmap word per lane and per thread");
+  __shared__ uint32_t s_bin[kBins];
   __shared__ uint32_t s_cand[kCand];
+  __shared__ uint64_t s_gt[kWords];
+  __shared__ uint64_t s_eq[kWords];
   __shared__ __align__(16) uint32_t hist[kKthHist];
   __shared__ int s_scan[2 * kTkWaves];
   __shared__ uint32_t s_red[2 * kTkWaves];
+  __shared__ int s_wc[kTkWaves];
   __shared__ uint32_t s_bstar;
   __shared__ int s_need;
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -337,26 +357,19 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_lds_kernel(const float* _
     return;
   }
   if (K == 0) return;
-  // 1. codes into LDS (16 unconditional loads per thread in flight; indices
-  //    past the row re-read its last key) and their range
+  // 1. codes into registers
   const float* src = keys + size_t(row) * n + lo;
-  constexpr int LPT = 16;
+  const int wb = wave * 64 * PER + lane;       // this lane's first key
+  uint32_t u[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) u[e] = f32_order_key(src[min(wb + 64 * e, m - 1)]);
+  const int nfake = PER * kTkThreads - m;      // copies of the last key past the row end
+  const uint32_t ulast = f32_order_key(src[m - 1]);
   uint32_t cmin = 0xFFFFFFFFu, cmax = 0u;
-  for (int c0 = 0; c0 < m; c0 += kTkThreads * LPT) {
-    float v[LPT];
 #pragma unroll
-    for (int e = 0; e < LPT; ++e) {
-      const int i = c0 + e * kTkThreads + tid;
-      v[e] = src[i < m ? i : m - 1];
-    }
-#pragma unroll
-    for (int e = 0; e < LPT; ++e) {
-      const int i = c0 + e * kTkThreads + tid;
-      const uint32_t u = f32_order_key(v[e]);
-      if (i < m) s_code[lds_pad(i)] = u;
-      cmin = u < cmin ? u : cmin;              // the re-read last key is in range anyway
-      cmax = u > cmax ? u : cmax;
-    }
+  for (int e = 0; e < PER; ++e) {
+    cmin = u[e] < cmin ? u[e] : cmin;
+    cmax = u[e] > cmax ? u[e] : cmax;
   }
   for (int i = tid; i < kBins; i += kTkThreads) s_bin[i] = 0;
   cmin = wave_minmax_u32<false>(cmin);
@@ -377,8 +390,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_lds_kernel(const float* _
   //    and the bin b* holding the K-th largest
   const int wbits = 32 - __clz(cmax - cmin);
   const int sh = wbits > 12 ? wbits - 12 : 0;
-#pragma unroll 8
-  for (int i = tid; i < m; i += kTkThreads) atomicAdd(&s_bin[(s_code[lds_pad(i)] - cmin) >> sh], 1u);
+#pragma unroll
+  for (int e = 0; e < PER; ++e) atomicAdd(&s_bin[(u[e] - cmin) >> sh], 1u);
+  if (tid == 0 && nfake) atomicSub(&s_bin[(ulast - cmin) >> sh], uint32_t(nfake));
   __syncthreads();
   {
     constexpr int BT = kBins / kTkThreads;            // bins BT*t .. BT*t+BT-1
@@ -403,71 +417,89 @@ __global__ __launch_bounds__(kTkThreads) void topk_row_lds_kernel(const float* _
   __syncthreads();
   const uint32_t bstar = s_bstar;
   int need = s_need;
-  // 3. the codes of bin b* into a short list, chunk by chunk in order
-  const int W = (m + kTkThreads - 1) / kTkThreads;    // codes per thread chunk
-  const int j0 = tid * W, j1 = j0 + W < m ? j0 + W : m;
-  int mine = 0;
-#pragma unroll 8
-  for (int j = j0; j < j1; ++j) mine += ((s_code[lds_pad(j)] - cmin) >> sh) == bstar;
-  int ncand;
-  int slot = block_scan1<false>(mine, ncand, s_scan);   // a barrier follows
-  if (ncand <= kCand && mine) {
-#pragma unroll 8
-    for (int j = j0; j < j1; ++j) {
-      const uint32_t u = s_code[lds_pad(j)];
-      if (((u - cmin) >> sh) == bstar) s_cand[slot++] = u;
+  // 3. the codes of bin b* into a short list in index order (the copies of
+  //    the last key, if they fall in b*, are its tail and are cut off)
+  int c = 0;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) c += __popcll(__ballot(((u[e] - cmin) >> sh) == bstar));
+  if (lane == 0) s_wc[wave] = c;
+  __syncthreads();
+  int off = 0, ncand = 0;
+#pragma unroll
+  for (int w = 0; w < kTkWaves; ++w) {
+    const int v = s_wc[w];
+    off += w < wave ? v : 0;
+    ncand += v;
+  }
+  if (ncand > kCand) {                                // a crowded bin: the row path
+    topk_row<SDQ_KEY_F32_MAX>(keys, size_t(row) * n, n, k, n_sink, n_local, o, stride);
+    return;
+  }
+  {
+    const uint32_t blo = cmin + (bstar << sh);        // bin b* is [blo, blo + 2^sh)
+    const uint32_t bw = sh >= 32 ? 0xFFFFFFFFu : (1u << sh);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const bool in = u[e] - blo < bw;
+      const uint64_t mk = __ballot(in);
+      if (in) s_cand[off + lanes_below(mk)] = u[e];
+      off += __popcll(mk);
     }
   }
+  if (((ulast - cmin) >> sh) == bstar) ncand -= nfake;
   __syncthreads();
   // 4. the exact K-th code and how many of its ties to keep (all codes above
   //    bin b* are in the top K already)
-  KthResult kr;
-  if (ncand <= kCand) {
-    kr = select_kth(
-        ncand, need,
-        [&](int i, uint32_t* u) {
-          *u = s_cand[i];
-          return true;
-        },
-        hist, s_red);
-  } else {                                            // a crowded bin: every code
-    kr = select_kth(
-        m, K,
-        [&](int i, uint32_t* u) {
-          *u = s_code[lds_pad(i)];
-          return true;
-        },
-        hist, s_red);
-  }
+  const KthResult kr = select_kth(
+      ncand, need,
+      [&](int i, uint32_t* v) {
+        *v = s_cand[i];
+        return true;
+      },
+      hist, s_red);
   const uint32_t T = kr.T;
   need = kr.need;
-  // 5. winners in index order: every code above T, and the first `need`
-  //    codes equal to T
-  int gt = 0, eq = 0;
-#pragma unroll 8
-  for (int j = j0; j < j1; ++j) {
-    const uint32_t u = s_code[lds_pad(j)];
-    gt += u > T;
-    eq += u == T;
-  }
-  int egt, eeq, tgt, teq;
-  block_scan2<false>(gt, eq, egt, eeq, tgt, teq, s_scan);   // last use of s_scan
-  int pos = n_sink + egt + (eeq < need ? eeq : need);
-  int my_eq = eeq;
-  const int end = n_sink + K;
-#pragma unroll 8
-  for (int j = j0; j < j1; ++j) {
-    const uint32_t u = s_code[lds_pad(j)];
-    if (u > T) {
-      if (pos < end) o[pos] = lo + j;
-      ++pos;
-    } else if (u == T) {
-      if (my_eq < need) {
-        if (pos < end) o[pos] = lo + j;
-        ++pos;
-      }
-      ++my_eq;
+  // 5. bitmaps of the codes above T and equal to T; lane e of the wave keeps
+  //    the two ballots of its e-th keys
+  uint32_t glo = 0, ghi = 0, qlo = 0, qhi = 0;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const uint64_t gm = __ballot(u[e] > T);
+    const uint64_t qm = __ballot(u[e] == T);
+    if (lane == e) {
+      glo = uint32_t(gm);
+      ghi = uint32_t(gm >> 32);
+      qlo = uint32_t(qm);
+      qhi = uint32_t(qm >> 32);
     }
+  }
+  if (lane < PER) {
+    s_gt[wave * PER + lane] = (uint64_t(ghi) << 32) | glo;
+    s_eq[wave * PER + lane] = (uint64_t(qhi) << 32) | qlo;
+  }
+  __syncthreads();
+  // thread t takes word t: keys 64 PER (t / PER) + 64 (t % PER) + [0, 64)
+  const uint64_t gw = tid < kWords ? s_gt[tid] : 0ull;
+  uint64_t qw = tid < kWords ? s_eq[tid] : 0ull;
+  int gb, qb, gtot, qtot;
+  block_scan2<false>(__popcll(gw), __popcll(qw), gb, qb, gtot, qtot, s_scan);
+  int take = need - qb;                               // ties of this word that are kept
+  take = take < 0 ? 0 : take;
+  uint64_t qkeep = 0;
+  for (int j = 0; j < take && qw; ++j) {
+    const uint64_t b = qw & (~qw + 1);
+    qkeep |= b;
+    qw ^= b;
+  }
+  uint64_t bits = gw | qkeep;
+  int pos = n_sink + gb + (qb < need ? qb : need);
+  const int i0 = lo + (tid / PER) * 64 * PER + (tid % PER) * 64;
+  const int end = n_sink + K;
+  while (bits) {
+    const int b = __ffsll((unsigned long long)bits) - 1;
+    if (pos < end) o[pos] = i0 + b;
+    ++pos;
+    bits &= bits - 1;
   }
 }
 
@@ -1483,13 +1515,23 @@ static int topk_select_launch(const char* nm, const void* keys, int key_type, in
     return check_launch(nm);
   }
   const int m_comp = n - n_sink - n_local;
-  if (key_type == SDQ_KEY_F32_MAX && m_comp > kRowLdsMin && m_comp <= kRowLdsSmall)
-    hipLaunchKernelGGL(topk_row_lds_kernel<kRowLdsSmall>, dim3(rows), dim3(kTkThreads), 0, stream,
-                       fk, n, k, n_sink, n_local, idx_out, stride);
-  else if (key_type == SDQ_KEY_F32_MAX && m_comp > kRowLdsMin && m_comp <= kRowLdsMax)
-    hipLaunchKernelGGL(topk_row_lds_kernel<kRowLdsMax>, dim3(rows), dim3(kTkThreads), 0, stream,
-                       fk, n, k, n_sink, n_local, idx_out, stride);
-  else if (key_type == SDQ_KEY_F32_MAX)
+  if (key_type == SDQ_KEY_F32_MAX && m_comp > kRowRegMin && m_comp <= kRowRegMax) {
+    if (m_comp <= 2048)
+      hipLaunchKernelGGL(topk_row_reg_kernel<2048>, dim3(rows), dim3(kTkThreads), 0, stream, fk, n,
+                         k, n_sink, n_local, idx_out, stride);
+    else if (m_comp <= 4096)
+      hipLaunchKernelGGL(topk_row_reg_kernel<4096>, dim3(rows), dim3(kTkThreads), 0, stream, fk, n,
+                         k, n_sink, n_local, idx_out, stride);
+    else if (m_comp <= 8192)
+      hipLaunchKernelGGL(topk_row_reg_kernel<8192>, dim3(rows), dim3(kTkThreads), 0, stream, fk, n,
+                         k, n_sink, n_local, idx_out, stride);
+    else if (m_comp <= 16384)
+      hipLaunchKernelGGL(topk_row_reg_kernel<16384>, dim3(rows), dim3(kTkThreads), 0, stream, fk, n,
+                         k, n_sink, n_local, idx_out, stride);
+    else
+      hipLaunchKernelGGL(topk_row_reg_kernel<kRowRegMax>, dim3(rows), dim3(kTkThreads), 0, stream,
+                         fk, n, k, n_sink, n_local, idx_out, stride);
+  } else if (key_type == SDQ_KEY_F32_MAX)
     hipLaunchKernelGGL(topk_row_kernel<SDQ_KEY_F32_MAX>, dim3(rows), dim3(kTkThreads), 0, stream,
                        keys, n, k, n_sink, n_local, idx_out, stride);
   else

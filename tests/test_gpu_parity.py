@@ -295,7 +295,11 @@ def _topk_ref(keys, k, n_sink, n_local, largest):
                                             (2, 200000, 3000, 128, 128), (3, 300, 0, 5, 5),
                                             (8, 32768, 512, 0, 0), (2, 32788, 300, 10, 10),
                                             (2, 32809, 100, 20, 20), (3, 40000, 2000, 0, 0),
-                                            (2, 16384, 16383, 0, 0), (1, 32768, 32768, 0, 0)])
+                                            (2, 16384, 16383, 0, 0), (1, 32768, 32768, 0, 0),
+                                            (2, 1025, 1024, 0, 0), (4, 1500, 100, 0, 0),
+                                            (3, 2048, 2047, 0, 0), (2, 3000, 64, 5, 7),
+                                            (2, 6000, 700, 0, 0), (2, 12000, 1000, 64, 64),
+                                            (2, 20000, 1, 0, 0), (3, 8192, 4000, 0, 0)])
 def test_topk_f32_bitexact(sdq, rows, n, k, ns, nl):
     _say(f"topk f32 rows={rows} n={n} k={k}")
     g = np.random.default_rng(n + k)
@@ -319,9 +323,9 @@ def test_topk_f32_degenerate_rows(sdq):
     keys[0, 99999] = 7.0
     got = host(sdq.topk_select(dev(keys), 9000, 1, 1))
     assert np.array_equal(got, _topk_ref(keys, 9000, 1, 1, True))
-    # rows held in LDS (at most 32768 competing keys): all tied, -inf pads,
-    # a single distinct key
-    for n2 in (32768, 4096):
+    # rows held in registers (at most 32768 competing keys, ragged lengths
+    # included): all tied, -inf pads, a single distinct key
+    for n2 in (32768, 4096, 1500, 6000, 20001):
         keys = np.zeros((3, n2), np.float32)
         keys[1, n2 - 27:] = -np.inf
         keys[2, :] = 1.5
