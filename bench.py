@@ -6,7 +6,7 @@ The timed step is one decode step of one layer of the bit-plane index at a
 plan of B = 56 plane bits per KV head, k = 512 selected rows per KV head:
 
     fathom_plan -> fathom_scan (+ 64-token block maxima)
-                -> topk_select_block_max -> gather_attend
+                -> topk_select_block_max_split -> gather_attend
 
 All inputs are seeded synthetic data (synth.fathom_case(3)) resident in HBM
 before timing starts.  Eight copies of the plane index and of the K/V cache
@@ -287,6 +287,7 @@ def main():
     idx = torch.empty(G, k, dtype=torch.int32, device=dev)
     out = torch.empty(1, G * Hgrp, 128, device=dev)
     ws = lib.attend_workspace(1, G * Hgrp, G, False, k, 1, dev)
+    ws_bm = lib.topk_bm_split_workspace(G, n, dev)
     q3, K4, V4, idx3 = q.view(1, G * Hgrp, 128), KC[0], VC[0], idx.view(1, G, k)
     torch.cuda.synchronize()
 
@@ -302,7 +303,7 @@ def main():
         plan_scan(i)
         if ev:
             ev[1].record()
-        lib.topk_select_block_max(scores, bmax, k, idx=idx)
+        lib.topk_select_block_max_split(scores, bmax, k, idx=idx, ws=ws_bm)
         if ev:
             ev[2].record()
         lib.gather_attend(q3, KC[i % N_COPIES], VC[i % N_COPIES], idx3, out=out, ws=ws)
@@ -588,16 +589,17 @@ def run_extras(torch, np, lib, bytemodel, synth, dev, case, K4, V4, q, var, q3, 
     bm_r = torch.empty(G, n // 64, device=dev)
     idx_r = torch.empty(G, k + 64, dtype=torch.int32, device=dev)
     ws_r = lib.attend_workspace(1, G * Hgrp, G, False, k + 64, 1, dev)
+    ws_bm = lib.topk_bm_split_workspace(G, n, dev)
     out_r = torch.empty_like(q3)
 
     def ragged(i):
         lib.fathom_plan_scan(index, q, var, 56, n_r, planes=P[i % len(P)], meta=M[i % len(M)],
                              scores=sc_r, block_max=bm_r, write_plan=False)
-        lib.topk_select_block_max(sc_r, bm_r, k, n_local=64, idx=idx_r)
+        lib.topk_select_block_max_split(sc_r, bm_r, k, n_local=64, idx=idx_r, ws=ws_bm)
         lib.gather_attend(q3, K4, V4, idx_r.view(1, G, -1), out=out_r, ws=ws_r, n=n_r)
     ex["decode_step_ragged_us"] = round(timeit_graph(torch, ragged), 2)
     log(f"extras: ragged step {ex['decode_step_ragged_us']} us")
-    del sc_r, bm_r, idx_r, ws_r, out_r
+    del sc_r, bm_r, idx_r, ws_r, out_r, ws_bm
 
     # read-plan quality on this layer: sparse vs dense attention error, needle and
     # exact top-k recall, scan bytes per plan

@@ -277,6 +277,24 @@ int topk_select_noalloc(const void* keys, int key_type, int rows, int n, int k, 
 int topk_select_block_max(const float* keys, const float* block_max, int rows, int n, int k,
                           int n_sink, int n_local, int32_t* idx_out, hipStream_t stream);
 
+/* topk_select_block_max_split -- topk_select_block_max with each row's
+ * candidate gather spread over several workgroups (same sources, arguments,
+ * ordering, windows and output).  Every workgroup of a row derives the same
+ * threshold from the block maxima and reads its share of the candidate
+ * blocks; their candidates meet in the workspace, and a second launch
+ * selects exactly among them.  Rows whose candidates overflow a share take
+ * the exact row path, as in topk_select_block_max.
+ *   ws, ws_bytes  workspace of at least
+ *             topk_select_block_max_split_workspace_bytes(rows, n) bytes,
+ *             16-byte aligned; its contents on entry do not matter and calls
+ *             on one workspace must not overlap.
+ * Errors: those of topk_select_block_max, plus SDQ_EINVAL on a null or short
+ * workspace or rows > 65535. */
+size_t topk_select_block_max_split_workspace_bytes(int rows, int n);
+int topk_select_block_max_split(const float* keys, const float* block_max, int rows, int n, int k,
+                                int n_sink, int n_local, int32_t* idx_out, void* ws,
+                                size_t ws_bytes, hipStream_t stream);
+
 /* hamming_scan -- dist[h][i] = popcount(sigs[h][i] XOR qsig[h]) in [0, 32]
  * (HashAttention study notes, sec. 2.2).
  *   sigs uint32 [H][n_cap] (rows of a growing cache, the first n scored);

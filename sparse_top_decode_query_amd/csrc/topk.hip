@@ -21,7 +21,9 @@
 //    (one workgroup per row), or, for long rows, per-segment histograms in
 //    the workspace let one workgroup per segment place its own winners.
 //  * block-max path (topk_select_block_max): float32 rows whose 64-key block
-//    maxima are known read only the blocks that can hold a winner.
+//    maxima are known read only the blocks that can hold a winner.  Its split
+//    form (topk_select_block_max_split) spreads each row's candidate gather
+//    over several workgroups and selects in a second launch.
 //  * fast path for long float32 rows (many workgroups per row): one pass
 //    builds a 2048-bin histogram of the top 11 bits of u, a tiny kernel picks
 //    the bin holding the k-th code, a second pass appends every element of
@@ -1154,31 +1156,21 @@ __device__ __forceinline__ float f32_from_order_key(uint32_t c) {
 }
 
 
-__global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __restrict__ keys,
-                                                             const float* __restrict__ bm, int n,
-                                                             int nb, int k, int n_sink, int n_local,
-                                                             int32_t* __restrict__ out, int stride) {
-  __shared__ __align__(16) uint32_t sbin[kBmBins];
-  __shared__ int cb[kBmCandBlocks];       // candidate block numbers, ascending
-  __shared__ int s_cnt[640];              // kept keys per block of a chunk, then offsets
-  __shared__ float ckey[kBmCap];
-  __shared__ int cidx[kBmCap];
-  __shared__ __align__(16) uint32_t hist[kKthHist];
-  __shared__ uint32_t s_red[2 * kTkWaves];
-  __shared__ int s_scan[4 * kTkWaves];    // two buffers: scans alternate
-  __shared__ uint32_t s_thr;
-  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int32_t* o = out + size_t(row) * stride;
-  const int lo = n_sink, hi = n - n_local, m = hi - lo;
-  const int blo = lo / 64, nbc = m / 64;        // competition blocks [blo, blo + nbc)
-  const int K = k < m ? k : m;
-  const size_t base = size_t(row) * n;
-  if (K == m || K == 0 || K > nbc) {
-    topk_row<SDQ_KEY_F32_MAX>(keys, base, n, k, n_sink, n_local, o, stride);
-    return;
-  }
+// Candidate keys kept as floats (converted to order codes when read: cheaper
+// in the collection loop) or as order codes (the split form's workspace).
+__device__ __forceinline__ uint32_t ckey_code(uint32_t c) { return c; }
+__device__ __forceinline__ uint32_t ckey_code(float v) { return f32_order_key(v); }
+// Phases 1-3 of the block-max path for one row (all threads of the
+// workgroup call it): the threshold thr <= the K-th largest key from the
+// row's block maxima brow[0..nbc), and the blocks whose maximum reaches it,
+// in index order, in cb[0..ncb).  Returns false (cb not written) when more
+// than kBmCandBlocks blocks qualify.
+__device__ __forceinline__ bool bm_candidate_blocks(const float* __restrict__ brow, int nbc, int K,
+                                                    uint32_t* sbin, int* cb, uint32_t* s_red,
+                                                    int* s_scan, uint32_t* s_thr, float& thr_out,
+                                                    int& ncb_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // 1. this thread's block maxima (blocks past the end read as -inf)
-  const float* brow = bm + size_t(row) * nb + blo;
   const int b0 = tid * kBmPer;
   float mx[kBmPer];
   if ((reinterpret_cast<uintptr_t>(brow) & 15) == 0 && b0 + kBmPer <= nbc) {
@@ -1240,34 +1232,46 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __rest
     int above = tot - before - lsum;                     // maxima in higher threads' bins
 #pragma unroll
     for (int e = BT - 1; e >= 0; --e) {
-      if (above < K && above + cnt[e] >= K) s_thr = cmin + (uint32_t(BT * tid + e) << sh);
+      if (above < K && above + cnt[e] >= K) (*s_thr) = cmin + (uint32_t(BT * tid + e) << sh);
       above += cnt[e];
     }
   }
   __syncthreads();
-  const float thr = f32_from_order_key(s_thr);          // v >= thr  <=>  bin(v) >= b*
+  const float thr = f32_from_order_key(*s_thr);          // v >= thr  <=>  bin(v) >= b*
+  thr_out = thr;
   // 3. candidate blocks in index order
   uint32_t flags = 0;
 #pragma unroll
   for (int u = 0; u < kBmPer; ++u) flags |= uint32_t(mx[u] >= thr) << u;   // -inf never passes
   int ncb;
   const int cpos = block_scan1<false>(__popc(flags), ncb, s_scan);   // a barrier follows
-  if (ncb > kBmCandBlocks) {
-    topk_row<SDQ_KEY_F32_MAX>(keys, base, n, k, n_sink, n_local, o, stride);
-    return;
-  }
+  ncb_out = ncb;
+  if (ncb > kBmCandBlocks) return false;
   {
     int pos = cpos;
     for (uint32_t f = flags; f; f &= f - 1) cb[pos++] = b0 + __ffs(f) - 1;
   }
   __syncthreads();
+  return true;
+}
+
+// Phase 4: the keys >= thr of the candidate blocks cb[0..ncb) (block
+// numbers from blo), in index order, into ckey and their indices into cidx
+// (both of `cap` entries).  Returns their count; when it exceeds
+// cap nothing more is written (the caller then falls back).  kRC rounds of
+// 32 blocks are in flight at once; s_cnt holds 32 kRC entries.
+template <int kRC>
+__device__ __forceinline__ int bm_collect(const float* __restrict__ keys, size_t base, int blo,
+                                          const int* cb, int ncb, float thr, float* ckey, int* cidx,
+                                          int cap, int* s_cnt,
+                          int* s_scan) {
+  const int tid = threadIdx.x;
   // 4. candidate keys in index order.  16 lanes share a block (lane q holds
   //    its keys 4q..4q+3), so a wave load covers four whole blocks; a chunk
   //    of kRC rounds x 32 blocks is in flight at once.  Per-lane counts of
   //    keys >= thr travel four rounds to an int in 8-bit fields through the
   //    in-group sums and prefixes; a prefix sum over the chunk's blocks
   //    places them.
-  constexpr int kRC = 20;                               // rounds per chunk (640 blocks)
   constexpr int kPk = kRC / 4;                          // packed counters
   const int grp = tid >> 4, q = tid & 15;
   int nc = 0;
@@ -1323,7 +1327,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __rest
       nc += tot;
     }
     __syncthreads();
-    if (nc <= kBmCap) {
+    if (nc <= cap) {
       int offs[kRC], firsts[kRC];                       // every LDS read issued up front
 #pragma unroll
       for (int r = 0; r < kRC; ++r) {
@@ -1356,15 +1360,23 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __rest
     }
     __syncthreads();
   }
-  if (nc > kBmCap || nc < K) {
-    topk_row<SDQ_KEY_F32_MAX>(keys, base, n, k, n_sink, n_local, o, stride);
-    return;
-  }
+  return nc;
+}
+
+// Phases 5-6: the exact K-th largest of the candidate keys ckey[0..nc)
+// (index order, indices in cidx) and its tie count, then the winners written
+// in index order, after the fixed windows.
+template <typename CK>
+__device__ __forceinline__ void bm_select_write(const CK* ckey, const int* cidx, int nc, int K,
+                                                int n,
+                                int n_sink, int n_local, int stride, int32_t* __restrict__ o,
+                                uint32_t* hist, uint32_t* s_red, int* s_scan) {
+  const int tid = threadIdx.x;
   // 5. exact K-th largest candidate code and how many of its ties to keep
   const KthResult kr = select_kth(
       nc, K,
       [&](int i, uint32_t* u) {
-        *u = f32_order_key(ckey[i]);
+        *u = ckey_code(ckey[i]);
         return true;
       },
       hist, s_red);
@@ -1379,7 +1391,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __rest
 #pragma unroll
     for (int e = 0; e < IPT; ++e) {
       const int i = i0 + e;
-      u[e] = i < nc ? f32_order_key(ckey[i]) : 0u;
+      u[e] = i < nc ? ckey_code(ckey[i]) : 0u;
       if (i < nc) {
         gt += u[e] > kr.T;
         eq += u[e] == kr.T;
@@ -1411,6 +1423,174 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __rest
     out_pos += tgt + (teq < eq_left ? teq : eq_left);
     eq_seen += teq;
   }
+}
+
+__global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __restrict__ keys,
+                                                             const float* __restrict__ bm, int n,
+                                                             int nb, int k, int n_sink, int n_local,
+                                                             int32_t* __restrict__ out, int stride) {
+  __shared__ __align__(16) uint32_t sbin[kBmBins];
+  __shared__ int cb[kBmCandBlocks];       // candidate block numbers, ascending
+  __shared__ int s_cnt[640];              // kept keys per block of a chunk, then offsets
+  __shared__ float ckey[kBmCap];
+  __shared__ int cidx[kBmCap];
+  __shared__ __align__(16) uint32_t hist[kKthHist];
+  __shared__ uint32_t s_red[2 * kTkWaves];
+  __shared__ int s_scan[4 * kTkWaves];    // two buffers: scans alternate
+  __shared__ uint32_t s_thr;
+  const int row = blockIdx.x;
+  int32_t* o = out + size_t(row) * stride;
+  const int lo = n_sink, hi = n - n_local, m = hi - lo;
+  const int blo = lo / 64, nbc = m / 64;        // competition blocks [blo, blo + nbc)
+  const int K = k < m ? k : m;
+  const size_t base = size_t(row) * n;
+  if (K == m || K == 0 || K > nbc) {
+    topk_row<SDQ_KEY_F32_MAX>(keys, base, n, k, n_sink, n_local, o, stride);
+    return;
+  }
+  float thr;
+  int ncb;
+  if (!bm_candidate_blocks(bm + size_t(row) * nb + blo, nbc, K, sbin, cb, s_red, s_scan, &s_thr,
+                           thr, ncb)) {
+    topk_row<SDQ_KEY_F32_MAX>(keys, base, n, k, n_sink, n_local, o, stride);
+    return;
+  }
+  const int nc = bm_collect<20>(keys, base, blo, cb, ncb, thr, ckey, cidx, kBmCap, s_cnt, s_scan);
+  if (nc > kBmCap || nc < K) {
+    topk_row<SDQ_KEY_F32_MAX>(keys, base, n, k, n_sink, n_local, o, stride);
+    return;
+  }
+  bm_select_write(ckey, cidx, nc, K, n, n_sink, n_local, stride, o, hist, s_red, s_scan);
+}
+
+// Split form (topk_select_block_max_split): kBmSegs workgroups per row each
+// derive the same threshold and candidate block list (phases 1-3 over all the
+// row's block maxima), collect the keys of their own contiguous share of the
+// list and leave them, in index order, in the workspace; one workgroup per
+// row then selects exactly among all of them and writes the winners.  The
+// candidate gather, one CU's load per row in the single-workgroup form, is
+// spread over kBmSegs CUs.
+constexpr int kBmSegs = 8;
+constexpr int kBmSegCap = 512;          // candidate keys per segment
+
+__host__ __device__ inline size_t bm_split_ws_per_row() {
+  return 64 + size_t(kBmSegs) * kBmSegCap * 8;
+}
+
+__global__ __launch_bounds__(kTkThreads) void topk_bm_seg_kernel(const float* __restrict__ keys,
+                                                                 const float* __restrict__ bm,
+                                                                 int n, int nb, int k, int n_sink,
+                                                                 int n_local, void* ws) {
+  __shared__ __align__(16) uint32_t sbin[kBmBins];
+  __shared__ int cb[kBmCandBlocks];
+  __shared__ int s_cnt[128];
+  __shared__ float ckey[kBmSegCap];
+  __shared__ int cidx[kBmSegCap];
+  __shared__ uint32_t s_red[2 * kTkWaves];
+  __shared__ int s_scan[4 * kTkWaves];
+  __shared__ uint32_t s_thr;
+  const int seg = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
+  char* wr = reinterpret_cast<char*>(ws) + size_t(row) * bm_split_ws_per_row();
+  int* count = reinterpret_cast<int*>(wr) + seg;
+  uint32_t* wcode = reinterpret_cast<uint32_t*>(wr + 64) + size_t(seg) * kBmSegCap;
+  int* widx = reinterpret_cast<int*>(wr + 64 + size_t(kBmSegs) * kBmSegCap * 4) +
+              size_t(seg) * kBmSegCap;
+  const int lo = n_sink, hi = n - n_local, m = hi - lo;
+  const int blo = lo / 64, nbc = m / 64;
+  const int K = k < m ? k : m;
+  const size_t base = size_t(row) * n;
+  if (K == m || K == 0 || K > nbc) {                    // the final kernel takes the row path
+    if (tid == 0) *count = -1;
+    return;
+  }
+  float thr;
+  int ncb;
+  if (!bm_candidate_blocks(bm + size_t(row) * nb + blo, nbc, K, sbin, cb, s_red, s_scan, &s_thr,
+                           thr, ncb)) {
+    if (tid == 0) *count = -1;
+    return;
+  }
+  const int j0 = int((long long)ncb * seg / kBmSegs), j1 = int((long long)ncb * (seg + 1) / kBmSegs);
+  int nc = 0;
+  if (j1 > j0)
+    nc = bm_collect<4>(keys, base, blo, cb + j0, j1 - j0, thr, ckey, cidx, kBmSegCap, s_cnt, s_scan);
+  if (nc > kBmSegCap) {
+    if (tid == 0) *count = -1;
+    return;
+  }
+  for (int i = tid; i < nc; i += kTkThreads) {
+    wcode[i] = f32_order_key(ckey[i]);
+    widx[i] = cidx[i];
+  }
+  if (tid == 0) *count = nc;
+}
+
+__global__ __launch_bounds__(kTkThreads) void topk_bm_final_kernel(const float* __restrict__ keys,
+                                                                   int n, int k, int n_sink,
+                                                                   int n_local, const void* ws,
+                                                                   int32_t* __restrict__ out,
+                                                                   int stride) {
+  __shared__ uint32_t ckey[kBmCap];
+  __shared__ int cidx[kBmCap];
+  __shared__ __align__(16) uint32_t hist[kKthHist];
+  __shared__ uint32_t s_red[2 * kTkWaves];
+  __shared__ int s_scan[4 * kTkWaves];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  int32_t* o = out + size_t(row) * stride;
+  const char* wr = reinterpret_cast<const char*>(ws) + size_t(row) * bm_split_ws_per_row();
+  const int* count = reinterpret_cast<const int*>(wr);
+  const uint32_t* wcode = reinterpret_cast<const uint32_t*>(wr + 64);
+  const int* widx = reinterpret_cast<const int*>(wr + 64 + size_t(kBmSegs) * kBmSegCap * 4);
+  const int lo = n_sink, hi = n - n_local, m = hi - lo;
+  const int K = k < m ? k : m;
+  // one round of loads: every segment's count, and the first kFirst keys of
+  // every segment (kTkThreads / kBmSegs threads a segment, two keys each);
+  // the slots past a segment's count are read but not used
+  constexpr int kTps = kTkThreads / kBmSegs;
+  constexpr int kFirst = 2 * kTps;
+  static_assert(kFirst <= kBmSegCap, "first round within a segment's slots");
+  const int ms = tid / kTps, mj = 2 * (tid % kTps);
+  const uint2 mc = *reinterpret_cast<const uint2*>(wcode + size_t(ms) * kBmSegCap + mj);
+  const int2 mi = *reinterpret_cast<const int2*>(widx + size_t(ms) * kBmSegCap + mj);
+  int cnt[kBmSegs], nc = 0;
+  bool ok = true;
+#pragma unroll
+  for (int s = 0; s < kBmSegs; ++s) {
+    cnt[s] = count[s];
+    ok = ok && cnt[s] >= 0;
+    nc += cnt[s] > 0 ? cnt[s] : 0;
+  }
+  if (!ok || nc > kBmCap || nc < K) {
+    topk_row<SDQ_KEY_F32_MAX>(keys, size_t(row) * n, n, k, n_sink, n_local, o, stride);
+    return;
+  }
+  // every segment's keys, segment after segment: index order again
+  int moff = 0, mcnt = 0;
+#pragma unroll
+  for (int s = 0; s < kBmSegs; ++s) {
+    moff += s < ms ? cnt[s] : 0;
+    mcnt = s == ms ? cnt[s] : mcnt;
+  }
+  if (mj < mcnt) {
+    ckey[moff + mj] = mc.x;
+    cidx[moff + mj] = mi.x;
+  }
+  if (mj + 1 < mcnt) {
+    ckey[moff + mj + 1] = mc.y;
+    cidx[moff + mj + 1] = mi.y;
+  }
+  // the rest of segments longer than kFirst (rare)
+  int off = 0;
+#pragma unroll
+  for (int s = 0; s < kBmSegs; ++s) {
+    for (int i = kFirst + tid; i < cnt[s]; i += kTkThreads) {
+      ckey[off + i] = wcode[size_t(s) * kBmSegCap + i];
+      cidx[off + i] = widx[size_t(s) * kBmSegCap + i];
+    }
+    off += cnt[s];
+  }
+  __syncthreads();
+  bm_select_write(ckey, cidx, nc, K, n, n_sink, n_local, stride, o, hist, s_red, s_scan);
 }
 
 }  // namespace sdq
@@ -1659,4 +1839,36 @@ extern "C" int topk_select_block_max(const float* keys, const float* block_max, 
   if (stride == 0) return SDQ_OK;
   launch_block_max_select(keys, block_max, rows, n, k, n_sink, n_local, idx_out, stride, stream);
   return check_launch("topk_select_block_max");
+}
+
+extern "C" size_t topk_select_block_max_split_workspace_bytes(int rows, int n) {
+  if (rows < 1 || n < 1) return 0;
+  return size_t(rows) * bm_split_ws_per_row();
+}
+
+extern "C" int topk_select_block_max_split(const float* keys, const float* block_max, int rows,
+                                           int n, int k, int n_sink, int n_local,
+                                           int32_t* idx_out, void* ws, size_t ws_bytes,
+                                           hipStream_t stream) {
+  const char* nm = "topk_select_block_max_split";
+  int stride = 0;
+  const int rc = topk_validate(nm, keys, SDQ_KEY_F32_MAX, rows, n, k, n_sink, n_local, idx_out,
+                               &stride);
+  if (rc != SDQ_OK) return rc;
+  SDQ_REQUIRE(block_max, "%s: null block_max", nm);
+  SDQ_REQUIRE(n % 64 == 0 && n_sink % 64 == 0 && n_local % 64 == 0,
+              "%s: n, n_sink and n_local must be multiples of 64", nm);
+  SDQ_REQUIRE(n / 64 <= kBmMaxBlocks, "%s: n=%d exceeds %d", nm, n, kBmMaxBlocks * 64);
+  SDQ_REQUIRE(reinterpret_cast<uintptr_t>(keys) % 16 == 0, "%s: keys must be 16-byte aligned", nm);
+  SDQ_REQUIRE(rows <= 65535, "%s: rows=%d exceeds 65535", nm, rows);
+  const size_t need = topk_select_block_max_split_workspace_bytes(rows, n);
+  SDQ_REQUIRE(ws && ws_bytes >= need, "%s: workspace of %zu bytes needed, %zu given", nm, need,
+              ws_bytes);
+  SDQ_REQUIRE(reinterpret_cast<uintptr_t>(ws) % 16 == 0, "%s: ws must be 16-byte aligned", nm);
+  if (stride == 0) return SDQ_OK;
+  hipLaunchKernelGGL(topk_bm_seg_kernel, dim3(kBmSegs, rows), dim3(kTkThreads), 0, stream, keys,
+                     block_max, n, n / 64, k, n_sink, n_local, ws);
+  hipLaunchKernelGGL(topk_bm_final_kernel, dim3(rows), dim3(kTkThreads), 0, stream, keys, n, k,
+                     n_sink, n_local, ws, idx_out, stride);
+  return check_launch(nm);
 }

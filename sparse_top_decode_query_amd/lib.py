@@ -38,6 +38,9 @@ _SIGS = {
     "fathom_plan_scan": ([_vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp,
                           _vp, _vp, _vp, _vp], _c_int),
     "topk_select_block_max": ([_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp], _c_int),
+    "topk_select_block_max_split": ([_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _c_size, _vp],
+                                    _c_int),
+    "topk_select_block_max_split_workspace_bytes": ([_c_int, _c_int], _c_size),
     "topk_select_workspace_bytes": ([_c_int, _c_int, _c_int, _c_int], _c_size),
     "topk_select": ([_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _c_size, _vp], _c_int),
     "topk_select_noalloc": ([_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp], _c_int),
@@ -310,6 +313,30 @@ def topk_select_block_max(keys, block_max, k, n_sink=0, n_local=0, idx=None, str
     _check(load().topk_select_block_max(_vp(keys.data_ptr()), _vp(block_max.data_ptr()), rows, n,
                                         int(k), int(n_sink), int(n_local), _vp(idx.data_ptr()),
                                         _stream(stream)), "topk_select_block_max")
+    return idx
+
+
+def topk_bm_split_workspace(rows, n, device="cuda"):
+    nbytes = int(load().topk_select_block_max_split_workspace_bytes(rows, n))
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def topk_select_block_max_split(keys, block_max, k, n_sink=0, n_local=0, idx=None, ws=None,
+                                stream=None):
+    """topk_select_block_max with each row's candidate gather spread over
+    several workgroups; ws from topk_bm_split_workspace (allocated here if
+    not given)."""
+    rows, n = keys.shape
+    _dev(keys, "keys", 4, rows * n)
+    _dev(block_max, "block_max", 4, rows * (n // 64))
+    idx = _out(idx, (rows, k + n_sink + n_local), torch.int32, keys.device, "idx", 4)
+    if ws is None:
+        ws = topk_bm_split_workspace(rows, n, keys.device)
+    _dev(ws, "ws", 1)
+    _check(load().topk_select_block_max_split(_vp(keys.data_ptr()), _vp(block_max.data_ptr()), rows,
+                                              n, int(k), int(n_sink), int(n_local),
+                                              _vp(idx.data_ptr()), _vp(ws.data_ptr()), ws.numel(),
+                                              _stream(stream)), "topk_select_block_max_split")
     return idx
 
 

@@ -69,6 +69,13 @@ def test_invalid_arguments_rejected_without_launch():
     assert L.topk_select_noalloc(p, 0, 512, 1 << 20, 512, 0, 0, p, s) == EINVAL  # beyond the scratch
     assert b"static scratch" in L.sdq_last_error()
     assert L.topk_select_noalloc(p, 7, 1, 10, 2, 0, 0, p, s) == EINVAL             # key type
+    ws_bm = L.topk_select_block_max_split_workspace_bytes(8, 1 << 20)
+    assert L.topk_select_block_max_split(p, p, 8, 1 << 20, 512, 0, 0, p, null, ws_bm, s) == EINVAL  # no ws
+    assert L.topk_select_block_max_split(p, p, 8, 1 << 20, 512, 0, 0, p, p, ws_bm - 1, s) == EINVAL  # short
+    assert b"workspace" in L.sdq_last_error()
+    assert L.topk_select_block_max_split(p, null, 8, 1 << 20, 512, 0, 0, p, p, ws_bm, s) == EINVAL  # bm
+    assert L.topk_select_block_max_split(p, p, 8, 1000, 512, 0, 0, p, p, ws_bm, s) == EINVAL  # n % 64
+    assert L.topk_select_block_max_split(p, p, 8, 1 << 21, 512, 0, 0, p, p, 1 << 30, s) == EINVAL  # > 2^20
     assert L.hamming_scan(p, p, 0, 10, 10, p, s) == EINVAL
     assert L.hamming_scan(p, p, 4, 11, 10, p, s) == EINVAL                   # n > n_cap
     assert L.hamming_scan_topk(p, p, 4, 11, 10, 2, 0, 0, p, p, p, 256, s) == EINVAL   # n > n_cap
@@ -96,6 +103,8 @@ def test_workspace_sizes():
     L = sdq.load()
     assert L.topk_select_workspace_bytes(8, 1 << 20, 512, 0) >= 8 * 8192 * 8
     assert L.topk_select_workspace_bytes(0, 10, 1, 0) == 0
+    assert L.topk_select_block_max_split_workspace_bytes(8, 1 << 20) >= 8 * 8 * 512 * 8
+    assert L.topk_select_block_max_split_workspace_bytes(0, 1 << 20) == 0
     ws = L.gather_attend_workspace_bytes(1, 32, 8, 0, 512, 1, 128)
     # 8 sets split in 4 parts of 128 rows: a partial per query head and part
     assert ws == 32 * 4 * 130 * 4

@@ -116,7 +116,8 @@ def test_fused_plan_scan_1m_all_heads(layer, budget, uniform):
     bm = torch.empty(G, n // 64, device="cuda")
     depth, qbar, scores = lib.fathom_plan_scan(layer["index"], layer["q"], layer["var"], budget, n,
                                                block_max=bm, uniform_channels=uniform)
-    idx = lib.topk_select_block_max(scores, bm, k)
+    idx = lib.topk_select_block_max_split(scores, bm, k)
+    assert torch.equal(idx, lib.topk_select_block_max(scores, bm, k))
     out = lib.gather_attend(layer["q"].view(1, G * 4, 128), layer["K"].view(1, G, n, 128),
                             layer["V"].view(1, G, n, 128), idx.view(1, G, k))
     # the two-call form (plan, then scan) gives the identical scores

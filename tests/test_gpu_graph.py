@@ -51,7 +51,7 @@ def _check_replays(step, outputs, replays=3):
 
 
 def test_fathom_step_graph_replay(sdq):
-    _say("bit-plane step: fused plan + scan, block-max top-k, attention")
+    _say("bit-plane step: fused plan + scan, split block-max top-k, attention")
     G, n, k = 8, 65536, 512
     case = synth.fathom_case(2, n=n)
     K = torch.from_numpy(case["K"].view(np.int16)).cuda()
@@ -64,10 +64,11 @@ def test_fathom_step_graph_replay(sdq):
     idx = torch.empty(G, k, dtype=torch.int32, device="cuda")
     out = torch.empty(1, G * 4, 128, device="cuda")
     ws = sdq.attend_workspace(1, G * 4, G, False, k, 1)
+    ws_bm = sdq.topk_bm_split_workspace(G, n)
 
     def step():
         sdq.fathom_plan_scan(index, q, var, 56, n, scores=scores, block_max=bm, write_plan=False)
-        sdq.topk_select_block_max(scores, bm, k, idx=idx)
+        sdq.topk_select_block_max_split(scores, bm, k, idx=idx, ws=ws_bm)
         sdq.gather_attend(q.view(1, G * 4, 128), K.view(1, G, n, 128), V.view(1, G, n, 128),
                           idx.view(1, G, k), out=out, ws=ws)
     _check_replays(step, [scores, bm, idx, out])

@@ -346,6 +346,7 @@ def test_topk_block_max_bitexact(sdq, rows, n, k, ns, nl):
     bm = kt.view(rows, n // 64, 64).amax(-1).contiguous()
     ref = _topk_ref(keys, k, ns, nl, True)
     assert np.array_equal(host(sdq.topk_select_block_max(kt, bm, k, ns, nl)), ref)
+    assert np.array_equal(host(sdq.topk_select_block_max_split(kt, bm, k, ns, nl)), ref)
     assert np.array_equal(host(sdq.topk_select(kt, k, ns, nl)), ref)
 
 
@@ -362,6 +363,7 @@ def test_topk_block_max_degenerate(sdq):
     for k in (1, 512, 2048):
         ref = _topk_ref(keys, k, 0, 0, True)
         assert np.array_equal(host(sdq.topk_select_block_max(kt, bm, k)), ref), k
+        assert np.array_equal(host(sdq.topk_select_block_max_split(kt, bm, k)), ref), k
         assert np.array_equal(host(sdq.topk_select(kt, k)), ref), k
 
 
