@@ -1163,12 +1163,13 @@ __device__ __forceinline__ uint32_t ckey_code(float v) { return f32_order_key(v)
 // Phases 1-3 of the block-max path for one row (all threads of the
 // workgroup call it): the threshold thr <= the K-th largest key from the
 // row's block maxima brow[0..nbc), and the blocks whose maximum reaches it,
-// in index order, in cb[0..ncb).  Returns false (cb not written) when more
+// in index order, in cb[0..ncb); cmax_out is the order code of the row's
+// largest key (its largest block maximum).  Returns false (cb not written) when more
 // than kBmCandBlocks blocks qualify.
 __device__ __forceinline__ bool bm_candidate_blocks(const float* __restrict__ brow, int nbc, int K,
                                                     uint32_t* sbin, int* cb, uint32_t* s_red,
                                                     int* s_scan, uint32_t* s_thr, float& thr_out,
-                                                    int& ncb_out) {
+                                                    int& ncb_out, uint32_t& cmax_out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // 1. this thread's block maxima (blocks past the end read as -inf)
   const int b0 = tid * kBmPer;
@@ -1211,6 +1212,7 @@ __device__ __forceinline__ bool bm_candidate_blocks(const float* __restrict__ br
     cmin = s_red[w] < cmin ? s_red[w] : cmin;
     cmax = s_red[kTkWaves + w] > cmax ? s_red[kTkWaves + w] : cmax;
   }
+  cmax_out = cmax;                                     // the row's largest key
   // bins of width 2^sh over [cmin, cmax]: (cmax - cmin) >> sh < kBmBins
   const int wbits = 32 - __clz(cmax - cmin);
   const int sh = wbits > 12 ? wbits - 12 : 0;
@@ -1363,23 +1365,15 @@ __device__ __forceinline__ int bm_collect(const float* __restrict__ keys, size_t
   return nc;
 }
 
-// Phases 5-6: the exact K-th largest of the candidate keys ckey[0..nc)
-// (index order, indices in cidx) and its tie count, then the winners written
-// in index order, after the fixed windows.
+// Phase 6: the winners in index order (candidates are already ordered by
+// index): every key above kr.T and the first kr.need equal to it, after the
+// fixed windows.
 template <typename CK>
-__device__ __forceinline__ void bm_select_write(const CK* ckey, const int* cidx, int nc, int K,
-                                                int n,
-                                int n_sink, int n_local, int stride, int32_t* __restrict__ o,
-                                uint32_t* hist, uint32_t* s_red, int* s_scan) {
+__device__ __forceinline__ void bm_write_winners(const CK* ckey, const int* cidx, int nc, int K,
+                                                 KthResult kr, int n, int n_sink, int n_local,
+                                                 int stride, int32_t* __restrict__ o,
+                                                 int* s_scan) {
   const int tid = threadIdx.x;
-  // 5. exact K-th largest candidate code and how many of its ties to keep
-  const KthResult kr = select_kth(
-      nc, K,
-      [&](int i, uint32_t* u) {
-        *u = ckey_code(ckey[i]);
-        return true;
-      },
-      hist, s_red);
   // 6. winners in index order (candidates are already ordered by index)
   write_fixed(o, n, n_sink, n_local, K, stride);
   int out_pos = n_sink, eq_seen = 0;
@@ -1425,6 +1419,23 @@ __device__ __forceinline__ void bm_select_write(const CK* ckey, const int* cidx,
   }
 }
 
+// Phases 5-6: the exact K-th largest of the candidate keys ckey[0..nc) and
+// its tie count, then the winners.
+template <typename CK>
+__device__ __forceinline__ void bm_select_write(const CK* ckey, const int* cidx, int nc, int K,
+                                                int n, int n_sink, int n_local, int stride,
+                                                int32_t* __restrict__ o, uint32_t* hist,
+                                                uint32_t* s_red, int* s_scan) {
+  const KthResult kr = select_kth(
+      nc, K,
+      [&](int i, uint32_t* u) {
+        *u = ckey_code(ckey[i]);
+        return true;
+      },
+      hist, s_red);
+  bm_write_winners(ckey, cidx, nc, K, kr, n, n_sink, n_local, stride, o, s_scan);
+}
+
 __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __restrict__ keys,
                                                              const float* __restrict__ bm, int n,
                                                              int nb, int k, int n_sink, int n_local,
@@ -1450,8 +1461,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __rest
   }
   float thr;
   int ncb;
+  uint32_t cmax;
   if (!bm_candidate_blocks(bm + size_t(row) * nb + blo, nbc, K, sbin, cb, s_red, s_scan, &s_thr,
-                           thr, ncb)) {
+                           thr, ncb, cmax)) {
     topk_row<SDQ_KEY_F32_MAX>(keys, base, n, k, n_sink, n_local, o, stride);
     return;
   }
@@ -1470,11 +1482,23 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __rest
 // row then selects exactly among all of them and writes the winners.  The
 // candidate gather, one CU's load per row in the single-workgroup form, is
 // spread over kBmSegs CUs.
+// Each segment also leaves a 256-bin histogram of its candidates' codes over
+// [code(thr), code of the row's largest key], a range every segment knows, so
+// the final kernel starts its exact search inside the bin of the K-th key.
+// Workspace per row: a 64-byte header (the segments' counts, then the two
+// range codes), the segments' codes, their indices, their histograms.
 constexpr int kBmSegs = 8;
 constexpr int kBmSegCap = 512;          // candidate keys per segment
+constexpr int kBmSegBins = 256;
 
 __host__ __device__ inline size_t bm_split_ws_per_row() {
-  return 64 + size_t(kBmSegs) * kBmSegCap * 8;
+  return 64 + size_t(kBmSegs) * (kBmSegCap * 8 + kBmSegBins * 4);
+}
+
+// bins of width 2^sh over [lo, hi]: (hi - lo) >> sh < kBmSegBins
+__device__ __forceinline__ int bm_seg_bin_shift(uint32_t lo, uint32_t hi) {
+  const int w = 32 - __clz(hi - lo);
+  return w > 8 ? w - 8 : 0;
 }
 
 __global__ __launch_bounds__(kTkThreads) void topk_bm_seg_kernel(const float* __restrict__ keys,
@@ -1489,12 +1513,17 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_seg_kernel(const float* __
   __shared__ uint32_t s_red[2 * kTkWaves];
   __shared__ int s_scan[4 * kTkWaves];
   __shared__ uint32_t s_thr;
+  __shared__ uint32_t s_h[kBmSegBins];
   const int seg = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
   char* wr = reinterpret_cast<char*>(ws) + size_t(row) * bm_split_ws_per_row();
   int* count = reinterpret_cast<int*>(wr) + seg;
   uint32_t* wcode = reinterpret_cast<uint32_t*>(wr + 64) + size_t(seg) * kBmSegCap;
   int* widx = reinterpret_cast<int*>(wr + 64 + size_t(kBmSegs) * kBmSegCap * 4) +
               size_t(seg) * kBmSegCap;
+  uint32_t* whist = reinterpret_cast<uint32_t*>(wr + 64 + size_t(kBmSegs) * kBmSegCap * 8) +
+                    size_t(seg) * kBmSegBins;
+  uint32_t* range = reinterpret_cast<uint32_t*>(wr) + kBmSegs;   // code(thr), row's largest
+  if (tid < kBmSegBins) s_h[tid] = 0;                 // the barriers below order this
   const int lo = n_sink, hi = n - n_local, m = hi - lo;
   const int blo = lo / 64, nbc = m / 64;
   const int K = k < m ? k : m;
@@ -1505,11 +1534,13 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_seg_kernel(const float* __
   }
   float thr;
   int ncb;
+  uint32_t cmax;
   if (!bm_candidate_blocks(bm + size_t(row) * nb + blo, nbc, K, sbin, cb, s_red, s_scan, &s_thr,
-                           thr, ncb)) {
+                           thr, ncb, cmax)) {
     if (tid == 0) *count = -1;
     return;
   }
+  const uint32_t tc = s_thr;
   const int j0 = int((long long)ncb * seg / kBmSegs), j1 = int((long long)ncb * (seg + 1) / kBmSegs);
   int nc = 0;
   if (j1 > j0)
@@ -1518,11 +1549,22 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_seg_kernel(const float* __
     if (tid == 0) *count = -1;
     return;
   }
+  const int hsh = bm_seg_bin_shift(tc, cmax);
   for (int i = tid; i < nc; i += kTkThreads) {
-    wcode[i] = f32_order_key(ckey[i]);
+    const uint32_t c = f32_order_key(ckey[i]);
+    wcode[i] = c;
     widx[i] = cidx[i];
+    atomicAdd(&s_h[(c - tc) >> hsh], 1u);               // tc <= c <= cmax
   }
-  if (tid == 0) *count = nc;
+  __syncthreads();
+  if (tid < kBmSegBins) whist[tid] = s_h[tid];
+  if (tid == 0) {
+    *count = nc;
+    if (seg == 0) {
+      range[0] = tc;
+      range[1] = cmax;
+    }
+  }
 }
 
 __global__ __launch_bounds__(kTkThreads) void topk_bm_final_kernel(const float* __restrict__ keys,
@@ -1535,12 +1577,15 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_final_kernel(const float* 
   __shared__ __align__(16) uint32_t hist[kKthHist];
   __shared__ uint32_t s_red[2 * kTkWaves];
   __shared__ int s_scan[4 * kTkWaves];
+  __shared__ int s_bin, s_need;
   const int row = blockIdx.x, tid = threadIdx.x;
   int32_t* o = out + size_t(row) * stride;
   const char* wr = reinterpret_cast<const char*>(ws) + size_t(row) * bm_split_ws_per_row();
   const int* count = reinterpret_cast<const int*>(wr);
   const uint32_t* wcode = reinterpret_cast<const uint32_t*>(wr + 64);
   const int* widx = reinterpret_cast<const int*>(wr + 64 + size_t(kBmSegs) * kBmSegCap * 4);
+  const uint32_t* whist = reinterpret_cast<const uint32_t*>(wr + 64 + size_t(kBmSegs) * kBmSegCap * 8);
+  const uint32_t* range = reinterpret_cast<const uint32_t*>(wr) + kBmSegs;
   const int lo = n_sink, hi = n - n_local, m = hi - lo;
   const int K = k < m ? k : m;
   // one round of loads: every segment's count, and the first kFirst keys of
@@ -1552,6 +1597,12 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_final_kernel(const float* 
   const int ms = tid / kTps, mj = 2 * (tid % kTps);
   const uint2 mc = *reinterpret_cast<const uint2*>(wcode + size_t(ms) * kBmSegCap + mj);
   const int2 mi = *reinterpret_cast<const int2*>(widx + size_t(ms) * kBmSegCap + mj);
+  uint32_t hb = 0;                                    // bin tid summed over the segments
+  if (tid < kBmSegBins) {
+#pragma unroll
+    for (int s = 0; s < kBmSegs; ++s) hb += whist[size_t(s) * kBmSegBins + tid];
+  }
+  const uint32_t tc = range[0], cmax = range[1];
   int cnt[kBmSegs], nc = 0;
   bool ok = true;
 #pragma unroll
@@ -1589,8 +1640,31 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_final_kernel(const float* 
     }
     off += cnt[s];
   }
+  // the bin holding the K-th largest candidate, from the summed histograms
+  // (the exact search's first pass, already done by the segments)
+  for (int i = tid; i < 2 * 256; i += kTkThreads) hist[i] = 0;
+  {
+    int tot;
+    const int before = block_scan1<false>(int(hb), tot, s_scan);   // a barrier follows
+    const int above = tot - before - int(hb);          // candidates in higher bins
+    if (tid < kBmSegBins && above < K && above + int(hb) >= K) {
+      s_bin = tid;
+      s_need = K - above;
+    }
+  }
   __syncthreads();
-  bm_select_write(ckey, cidx, nc, K, n, n_sink, n_local, stride, o, hist, s_red, s_scan);
+  const int hsh = bm_seg_bin_shift(tc, cmax);
+  const uint32_t blo = tc + (uint32_t(s_bin) << hsh);
+  const uint32_t span = hsh >= 32 ? 0xFFFFFFFFu : ((1u << hsh) - 1u);
+  const uint32_t bhi = cmax - blo > span ? blo + span : cmax;
+  const KthResult kr = select_kth_in(
+      nc, s_need,
+      [&](int i, uint32_t* u) {
+        *u = ckey[i];
+        return true;
+      },
+      hist, blo, bhi);
+  bm_write_winners(ckey, cidx, nc, K, kr, n, n_sink, n_local, stride, o, s_scan);
 }
 
 }  // namespace sdq
