@@ -5,7 +5,7 @@ The timed step is one decode step of one layer of the bit-plane index at a
 1,048,576-token context: 8 KV heads x 4 query heads (GQA), d = 128, a read
 plan of B = 56 plane bits per KV head, k = 512 selected rows per KV head:
 
-    fathom_plan -> fathom_scan (+ 64-token block maxima)
+    fathom_plan -> fathom_scan (+ 64-token block and 512-token group maxima)
                 -> topk_select_block_max_split -> gather_attend
 
 All inputs are seeded synthetic data (synth.fathom_case(3)) resident in HBM
@@ -284,6 +284,7 @@ def main():
     depth, qbar = lib.fathom_plan(q, var, B)
     scores = torch.empty(G, n, device=dev)
     bmax = torch.empty(G, n // 64, device=dev)
+    gmax = torch.empty(G, lib.n_groups(n), device=dev)
     idx = torch.empty(G, k, dtype=torch.int32, device=dev)
     out = torch.empty(1, G * Hgrp, 128, device=dev)
     ws = lib.attend_workspace(1, G * Hgrp, G, False, k, 1, dev)
@@ -294,7 +295,7 @@ def main():
     def plan_scan(i):
         # plan + scan in one launch (each scan workgroup derives its head's plan)
         lib.fathom_plan_scan(index, q, var, B, n, planes=P[i % N_COPIES], meta=M[i % N_COPIES],
-                             scores=scores, block_max=bmax, write_plan=False)
+                             scores=scores, block_max=bmax, write_plan=False, group_max=gmax)
 
     def step(i, ev=None):
         # ev (4 events) brackets every stage: used only by the stage breakdown
@@ -303,7 +304,7 @@ def main():
         plan_scan(i)
         if ev:
             ev[1].record()
-        lib.topk_select_block_max_split(scores, bmax, k, idx=idx, ws=ws_bm)
+        lib.topk_select_block_max_split(scores, bmax, k, idx=idx, ws=ws_bm, group_max=gmax)
         if ev:
             ev[2].record()
         lib.gather_attend(q3, KC[i % N_COPIES], VC[i % N_COPIES], idx3, out=out, ws=ws)
@@ -362,9 +363,11 @@ def main():
     scan_launch_us = timeit_graph(torch, plan_scan, reps=64, warm=5)
     sc_small = torch.empty(G, 64, device=dev)
     bm_small = torch.empty(G, 1, device=dev)
+    gm_small = torch.empty(G, 1, device=dev)
     scan_fixed_us = timeit_graph(torch, lambda i: lib.fathom_plan_scan(
-        index, q, var, 0, 64, scores=sc_small, block_max=bm_small, write_plan=False), reps=64, warm=5)
-    del sc_small, bm_small
+        index, q, var, 0, 64, scores=sc_small, block_max=bm_small, write_plan=False, group_max=gm_small),
+        reps=64, warm=5)
+    del sc_small, bm_small, gm_small
 
     # stage breakdown in a separate pass with every stage bracketed (context:
     # the extra events lengthen these steps)
@@ -408,7 +411,8 @@ def main():
     # the plain scan (plan read from a fathom_plan launch) as context
     plain_us = timeit_graph(torch, lambda i: lib.fathom_scan(index, depth, qbar, n, planes=P[i % N_COPIES],
                                                              meta=M[i % N_COPIES], scores=scores,
-                                                             block_max=bmax), reps=64, warm=5)
+                                                             block_max=bmax, group_max=gmax),
+                            reps=64, warm=5)
     plan_us = timeit_graph(torch, lambda i: lib.fathom_plan(q, var, B, depth=depth, qbar=qbar), reps=64, warm=5)
     roofline_plain = {"kernel": "fathom_scan (plan read)", "launch_us": round(plain_us, 2),
                       "frac": round(scan_bytes / (plain_us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
@@ -587,6 +591,7 @@ def run_extras(torch, np, lib, bytemodel, synth, dev, case, K4, V4, q, var, q3, 
     n_r = n - 27
     sc_r = torch.empty(G, n, device=dev)
     bm_r = torch.empty(G, n // 64, device=dev)
+    gm_r = torch.empty(G, lib.n_groups(n), device=dev)
     idx_r = torch.empty(G, k + 64, dtype=torch.int32, device=dev)
     ws_r = lib.attend_workspace(1, G * Hgrp, G, False, k + 64, 1, dev)
     ws_bm = lib.topk_bm_split_workspace(G, n, dev)
@@ -594,12 +599,12 @@ def run_extras(torch, np, lib, bytemodel, synth, dev, case, K4, V4, q, var, q3, 
 
     def ragged(i):
         lib.fathom_plan_scan(index, q, var, 56, n_r, planes=P[i % len(P)], meta=M[i % len(M)],
-                             scores=sc_r, block_max=bm_r, write_plan=False)
-        lib.topk_select_block_max_split(sc_r, bm_r, k, n_local=64, idx=idx_r, ws=ws_bm)
+                             scores=sc_r, block_max=bm_r, write_plan=False, group_max=gm_r)
+        lib.topk_select_block_max_split(sc_r, bm_r, k, n_local=64, idx=idx_r, ws=ws_bm, group_max=gm_r)
         lib.gather_attend(q3, K4, V4, idx_r.view(1, G, -1), out=out_r, ws=ws_r, n=n_r)
     ex["decode_step_ragged_us"] = round(timeit_graph(torch, ragged), 2)
     log(f"extras: ragged step {ex['decode_step_ragged_us']} us")
-    del sc_r, bm_r, idx_r, ws_r, out_r, ws_bm
+    del sc_r, bm_r, gm_r, idx_r, ws_r, out_r, ws_bm
 
     # read-plan quality on this layer: sparse vs dense attention error, needle and
     # exact top-k recall, scan bytes per plan

@@ -48,6 +48,9 @@ extern "C" {
 #define SDQ_ENOTSUP (-2)
 #define SDQ_EHIP (-3)
 
+/* 64-token blocks per group maximum (fathom_scan's group_max): 512 tokens */
+#define SDQ_GROUP_BLOCKS 8
+
 /* key kinds for topk_select */
 #define SDQ_KEY_F32_MAX 0 /* float32 scores, largest first        */
 #define SDQ_KEY_U8_MIN 1  /* uint8 distances, smallest first      */
@@ -58,7 +61,9 @@ const char* sdq_last_error(void);
 /* ABI version of this header (incremented on incompatible changes).
  * Version 2: row capacities (n_cap, nb_cap) on every call that reads
  * per-token cache arrays; fathom_append, minmax_append, oasis_select and
- * oasis_fetch. */
+ * oasis_fetch.
+ * Version 3: group maxima (SDQ_GROUP_BLOCKS blocks of 64 tokens) written by
+ * fathom_scan and fathom_plan_scan and read by topk_select_block_max_split. */
 int sdq_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -199,12 +204,16 @@ int fathom_gather(const uint32_t* planes_host, const uint32_t* meta_host, const 
  *                 an open block) are written as -inf
  *   block_max     float32 [G][n64/64] out, or NULL: the maximum score of
  *                 every 64-token block (input of topk_select_block_max)
+ *   group_max     float32 [G][ceil(n64/64 / SDQ_GROUP_BLOCKS)] out, or NULL:
+ *                 the maximum score of every group of SDQ_GROUP_BLOCKS
+ *                 blocks (the last group may be shorter); input of
+ *                 topk_select_block_max_split
  * Errors: SDQ_EINVAL on null pointers, G < 1, n_cap not a positive multiple
  * of 64, n outside [1, n_cap], n_cap >= 2^25 (one head's planes are addressed
  * with 31-bit offsets), d != 128, misaligned scores. */
 int fathom_scan(const uint32_t* planes, const uint32_t* meta, const uint8_t* depth,
                 const float* qbar, int G, int d, int n, int n_cap, float* scores,
-                float* block_max, hipStream_t stream);
+                float* block_max, float* group_max, hipStream_t stream);
 
 /* fathom_plan_scan -- fathom_plan (uniform == 0) or fathom_plan_uniform
  * (uniform != 0) followed by fathom_scan, in one launch (Fathom summary,
@@ -217,13 +226,13 @@ int fathom_scan(const uint32_t* planes, const uint32_t* meta, const uint8_t* dep
  *   budget                 budget_bits, or n_channels when uniform != 0
  *   planes, meta, G, d, n, n_cap  as fathom_scan
  *   depth, qbar            out, or both NULL: the plan, as fathom_plan writes it
- *   scores, block_max      as fathom_scan
+ *   scores, block_max, group_max  as fathom_scan
  * Errors: the union of fathom_plan's and fathom_scan's, and SDQ_EINVAL when
  * exactly one of depth and qbar is NULL. */
 int fathom_plan_scan(const float* q, const float* key_var, int H_grp, int budget, int uniform,
                      const uint32_t* planes, const uint32_t* meta, int G, int d, int n,
                      int n_cap, uint8_t* depth, float* qbar, float* scores, float* block_max,
-                     hipStream_t stream);
+                     float* group_max, hipStream_t stream);
 
 /* topk_select -- per-row top-k (HashAttention study notes, sec. 2.1 TOPK and
  * sec. 3.1 fixed positions; OasisKV review, per-KV-head top-K).
@@ -279,11 +288,20 @@ int topk_select_block_max(const float* keys, const float* block_max, int rows, i
 
 /* topk_select_block_max_split -- topk_select_block_max with each row's
  * candidate gather spread over several workgroups (same sources, arguments,
- * ordering, windows and output).  Every workgroup of a row derives the same
- * threshold from the block maxima and reads its share of the candidate
- * blocks; their candidates meet in the workspace, and a second launch
- * selects exactly among them.  Rows whose candidates overflow a share take
- * the exact row path, as in topk_select_block_max.
+ * ordering, windows and output).  The workgroups of a row derive the same
+ * threshold, at most the k-th largest score, and each collects the keys that
+ * reach it in its share of the row; their candidates meet in the workspace,
+ * and a second launch selects exactly among them.  With group maxima the
+ * threshold is the k-th largest maximum of the groups that lie wholly in the
+ * competing range (each such group holds a competing block with that
+ * maximum), and a workgroup reads only the block maxima of its own share;
+ * without them, or with fewer than k such groups, every workgroup derives
+ * the threshold from all of the row's block maxima.  Rows whose candidates
+ * overflow take the exact row path, as in topk_select_block_max.
+ *   block_max  as topk_select_block_max
+ *   group_max  float32 [rows][ceil(n/64 / SDQ_GROUP_BLOCKS)], or NULL:
+ *              group_max[r][j] = max of block_max[r][8j..8j+7] (of the
+ *              blocks that exist), as fathom_scan writes it
  *   ws, ws_bytes  workspace of at least
  *             topk_select_block_max_split_workspace_bytes(rows, n) bytes,
  *             16-byte aligned; its contents on entry do not matter and calls
@@ -291,9 +309,9 @@ int topk_select_block_max(const float* keys, const float* block_max, int rows, i
  * Errors: those of topk_select_block_max, plus SDQ_EINVAL on a null or short
  * workspace or rows > 65535. */
 size_t topk_select_block_max_split_workspace_bytes(int rows, int n);
-int topk_select_block_max_split(const float* keys, const float* block_max, int rows, int n, int k,
-                                int n_sink, int n_local, int32_t* idx_out, void* ws,
-                                size_t ws_bytes, hipStream_t stream);
+int topk_select_block_max_split(const float* keys, const float* block_max, const float* group_max,
+                                int rows, int n, int k, int n_sink, int n_local, int32_t* idx_out,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* hamming_scan -- dist[h][i] = popcount(sigs[h][i] XOR qsig[h]) in [0, 32]
  * (HashAttention study notes, sec. 2.2).

@@ -29,4 +29,4 @@ int check_launch(const char* what) {
 
 extern "C" const char* sdq_last_error(void) { return sdq::g_err; }
 
-extern "C" int sdq_abi_version(void) { return 2; }
+extern "C" int sdq_abi_version(void) { return 3; }

@@ -27,8 +27,9 @@
 // kernel's time by a sixth).
 //
 // Optionally the maximum score of every 64-token block is written as well
-// (the two lanes of a block combine theirs); top-k selection uses it to skip
-// blocks that cannot hold a winner.
+// (the two lanes of a block combine theirs), and the maximum of every group
+// of kGroupBlocks blocks (16 lanes combine theirs); top-k selection uses them
+// to skip blocks that cannot hold a winner.
 //
 // A growing cache: plane rows hold n_cap tokens, the first n are scored, and
 // n need not be a multiple of 64.  Score rows are n rounded up to 64 long;
@@ -41,6 +42,8 @@ namespace sdq {
 
 constexpr int kScanWaves = 4;
 constexpr int kTok = 32;                 // tokens per lane (one plane word)
+constexpr int kGroupBlocks = SDQ_GROUP_BLOCKS;   // 64-token blocks per group maximum
+static_assert(kGroupBlocks == 8, "a group is the 16 words of a quarter wave");
 
 template <int T>
 struct ChanData {
@@ -178,7 +181,8 @@ template <int MODE, bool SPLIT>
 __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
     const uint32_t* __restrict__ planes, const uint32_t* __restrict__ meta,
     const uint8_t* __restrict__ depth, const float* __restrict__ qbar, int n, int nb64, int n_cap,
-    float* __restrict__ scores, float* __restrict__ block_max, PlanIn pin) {
+    float* __restrict__ scores, float* __restrict__ block_max, float* __restrict__ group_max,
+    PlanIn pin) {
   __shared__ float s_q2[kHeadDim];
   __shared__ int s_j[kHeadDim];
   __shared__ int s_t[kHeadDim];
@@ -337,9 +341,17 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
     const int word = f >> 3;                                      // 8 float4 per word
     if (word < nvalid) dst[f] = so[word * 9 + (f & 7)];
   }
-  if (block_max) {
-    m = fmaxf(m, __shfl_xor(m, 1, 64));
-    if (valid && (lane & 1) == 0) block_max[size_t(g) * nb64 + b] = m;
+  if (block_max || group_max) {
+    m = fmaxf(m, __shfl_xor(m, 1, 64));                          // the block's two words
+    if (block_max && valid && (lane & 1) == 0) block_max[size_t(g) * nb64 + b] = m;
+    if (group_max) {
+      // 16 words from a multiple of 16: lanes past the end hold -inf
+      m = fmaxf(m, __shfl_xor(m, 2, 64));
+      m = fmaxf(m, __shfl_xor(m, 4, 64));
+      m = fmaxf(m, __shfl_xor(m, 8, 64));
+      const int ngr = (nb64 + kGroupBlocks - 1) / kGroupBlocks;
+      if (valid && (lane & 15) == 0) group_max[size_t(g) * ngr + (wd >> 4)] = m;
+    }
   }
 }
 
@@ -371,25 +383,25 @@ static int scan_checks(const char* nm, const uint32_t* planes, const uint32_t* m
 
 extern "C" int fathom_scan(const uint32_t* planes, const uint32_t* meta, const uint8_t* depth,
                            const float* qbar, int G, int d, int n, int n_cap, float* scores,
-                           float* block_max, hipStream_t stream) {
+                           float* block_max, float* group_max, hipStream_t stream) {
   SDQ_REQUIRE(depth && qbar, "fathom_scan: null pointer");
   if (const int rc = scan_checks("fathom_scan", planes, meta, G, d, n, n_cap, scores)) return rc;
   const int nb64 = (n + 63) / 64;
   if (scan_split(G, nb64))
     hipLaunchKernelGGL((fathom_scan_kernel<0, true>), dim3(cdiv(size_t(nb64) * 2, 64), G),
                        dim3(kScanWaves * 64), 0, stream, planes, meta, depth, qbar, n, nb64, n_cap,
-                       scores, block_max, PlanIn{});
+                       scores, block_max, group_max, PlanIn{});
   else
     hipLaunchKernelGGL((fathom_scan_kernel<0, false>), dim3(cdiv(size_t(nb64) * 2, kScanWaves * 64), G),
                        dim3(kScanWaves * 64), 0, stream, planes, meta, depth, qbar, n, nb64, n_cap,
-                       scores, block_max, PlanIn{});
+                       scores, block_max, group_max, PlanIn{});
   return check_launch("fathom_scan");
 }
 
 extern "C" int fathom_plan_scan(const float* q, const float* key_var, int H_grp, int budget,
                                 int uniform, const uint32_t* planes, const uint32_t* meta, int G,
                                 int d, int n, int n_cap, uint8_t* depth, float* qbar, float* scores,
-                                float* block_max, hipStream_t stream) {
+                                float* block_max, float* group_max, hipStream_t stream) {
   SDQ_REQUIRE(q && key_var, "fathom_plan_scan: null pointer");
   SDQ_REQUIRE((depth == nullptr) == (qbar == nullptr),
               "fathom_plan_scan: depth and qbar must both be given or both be null");
@@ -404,15 +416,15 @@ extern "C" int fathom_plan_scan(const float* q, const float* key_var, int H_grp,
   const dim3 block(kScanWaves * 64);
   if (uniform && split)
     hipLaunchKernelGGL((fathom_scan_kernel<2, true>), grid, block, 0, stream, planes, meta, nullptr,
-                       nullptr, n, nb64, n_cap, scores, block_max, pin);
+                       nullptr, n, nb64, n_cap, scores, block_max, group_max, pin);
   else if (uniform)
     hipLaunchKernelGGL((fathom_scan_kernel<2, false>), grid, block, 0, stream, planes, meta, nullptr,
-                       nullptr, n, nb64, n_cap, scores, block_max, pin);
+                       nullptr, n, nb64, n_cap, scores, block_max, group_max, pin);
   else if (split)
     hipLaunchKernelGGL((fathom_scan_kernel<1, true>), grid, block, 0, stream, planes, meta, nullptr,
-                       nullptr, n, nb64, n_cap, scores, block_max, pin);
+                       nullptr, n, nb64, n_cap, scores, block_max, group_max, pin);
   else
     hipLaunchKernelGGL((fathom_scan_kernel<1, false>), grid, block, 0, stream, planes, meta, nullptr,
-                       nullptr, n, nb64, n_cap, scores, block_max, pin);
+                       nullptr, n, nb64, n_cap, scores, block_max, group_max, pin);
   return check_launch("fathom_plan_scan");
 }

@@ -1160,6 +1160,45 @@ __device__ __forceinline__ float f32_from_order_key(uint32_t c) {
 // in the collection loop) or as order codes (the split form's workspace).
 __device__ __forceinline__ uint32_t ckey_code(uint32_t c) { return c; }
 __device__ __forceinline__ uint32_t ckey_code(float v) { return f32_order_key(v); }
+// The lower edge (an order code) of the kBmBins-bin histogram bin, over the
+// code range [cmin, cmax], that holds the K-th largest of the values v[u]
+// whose bit u of `in` is set (all threads of the workgroup call it; sbin
+// cleared before a barrier that precedes the call).  At least K values must
+// be counted; otherwise the result is cmin.
+template <int PER>
+__device__ __forceinline__ uint32_t bm_kth_bin_edge(const float (&v)[PER], uint32_t in, int K,
+                                                    uint32_t cmin, uint32_t cmax, uint32_t* sbin,
+                                                    int* s_scan, uint32_t* s_thr) {
+  const int tid = threadIdx.x;
+  // bins of width 2^sh over [cmin, cmax]: (cmax - cmin) >> sh < kBmBins
+  const int wbits = 32 - __clz(cmax - cmin);
+  const int sh = wbits > 12 ? wbits - 12 : 0;
+  if (tid == 0) *s_thr = cmin;
+#pragma unroll
+  for (int u = 0; u < PER; ++u)
+    if ((in >> u) & 1u) atomicAdd(&sbin[(f32_order_key(v[u]) - cmin) >> sh], 1u);
+  __syncthreads();
+  {
+    constexpr int BT = kBmBins / kTkThreads;           // bins BT*t .. BT*t+BT-1
+    int cnt[BT], lsum = 0;
+#pragma unroll
+    for (int e = 0; e < BT; ++e) {
+      cnt[e] = sbin[BT * tid + e];
+      lsum += cnt[e];
+    }
+    int tot;
+    const int before = block_scan1<false>(lsum, tot, s_scan);   // a barrier follows
+    int above = tot - before - lsum;                     // values in higher threads' bins
+#pragma unroll
+    for (int e = BT - 1; e >= 0; --e) {
+      if (above < K && above + cnt[e] >= K) (*s_thr) = cmin + (uint32_t(BT * tid + e) << sh);
+      above += cnt[e];
+    }
+  }
+  __syncthreads();
+  return *s_thr;
+}
+
 // Phases 1-3 of the block-max path for one row (all threads of the
 // workgroup call it): the threshold thr <= the K-th largest key from the
 // row's block maxima brow[0..nbc), and the blocks whose maximum reaches it,
@@ -1216,7 +1255,9 @@ __device__ __forceinline__ bool bm_candidate_blocks(const float* __restrict__ br
   // bins of width 2^sh over [cmin, cmax]: (cmax - cmin) >> sh < kBmBins
   const int wbits = 32 - __clz(cmax - cmin);
   const int sh = wbits > 12 ? wbits - 12 : 0;
-  // 2. histogram; bin b* holding the K-th largest maximum
+  // 2. histogram; bin b* holding the K-th largest maximum (the search of
+  //    bm_kth_bin_edge, written out here: called with 32 values a thread the
+  //    compiler scheduled the whole kernel 0.5 us slower)
 #pragma unroll
   for (int u = 0; u < kBmPer; ++u)
     if (b0 + u < nbc) atomicAdd(&sbin[(f32_order_key(mx[u]) - cmin) >> sh], 1u);
@@ -1476,20 +1517,30 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __rest
 }
 
 // Split form (topk_select_block_max_split): kBmSegs workgroups per row each
-// derive the same threshold and candidate block list (phases 1-3 over all the
-// row's block maxima), collect the keys of their own contiguous share of the
-// list and leave them, in index order, in the workspace; one workgroup per
+// derive the same threshold, collect the candidate keys of their own share of
+// the row and leave them, in index order, in the workspace; one workgroup per
 // row then selects exactly among all of them and writes the winners.  The
 // candidate gather, one CU's load per row in the single-workgroup form, is
-// spread over kBmSegs CUs.
+// spread over kBmSegs CUs.  With group maxima the threshold comes from those
+// (one value per kBmGrp blocks) and each workgroup lists the candidate blocks
+// of a contiguous eighth of the row from that eighth's block maxima, so no
+// workgroup reads all of the row's block maxima; without them (or with fewer
+// than K whole groups) every workgroup derives the threshold and the full
+// candidate block list from all block maxima (phases 1-3) and takes a
+// contiguous share of the list.  Any threshold <= the K-th largest key is
+// exact here: the final selection is exact over whatever the segments keep.
 // Each segment also leaves a 256-bin histogram of its candidates' codes over
 // [code(thr), code of the row's largest key], a range every segment knows, so
 // the final kernel starts its exact search inside the bin of the K-th key.
 // Workspace per row: a 64-byte header (the segments' counts, then the two
 // range codes), the segments' codes, their indices, their histograms.
 constexpr int kBmSegs = 8;
-constexpr int kBmSegCap = 512;          // candidate keys per segment
+constexpr int kBmSegCap = kBmCap;       // candidate keys per segment
 constexpr int kBmSegBins = 256;
+constexpr int kBmGrp = SDQ_GROUP_BLOCKS;          // blocks per group maximum
+constexpr int kBmGrpPer = kBmMaxBlocks / kBmGrp / kTkThreads;   // group maxima per thread
+constexpr int kBmSegPer = kBmMaxBlocks / kBmSegs / kTkThreads;  // a segment's blocks per thread
+static_assert(kBmGrpPer == 4 && kBmSegPer == 4, "one round of loads per thread");
 
 __host__ __device__ inline size_t bm_split_ws_per_row() {
   return 64 + size_t(kBmSegs) * (kBmSegCap * 8 + kBmSegBins * 4);
@@ -1501,8 +1552,82 @@ __device__ __forceinline__ int bm_seg_bin_shift(uint32_t lo, uint32_t hi) {
   return w > 8 ? w - 8 : 0;
 }
 
+// Threshold from the group maxima (all threads of the workgroup call it).
+// Groups [gi0, gi1) lie wholly inside the competition blocks: the K-th
+// largest of their maxima, T', is <= the K-th largest block maximum T (the K
+// groups whose maxima are >= T' each hold a competition block whose maximum
+// is their group's), so thr = the lower edge of the histogram bin holding T'
+// is a valid threshold, and it reads 16 times fewer values than T does.
+// Groups [gc0, gc1) meet the competition blocks: their largest maximum
+// bounds every competing key (cmax_out).  gi1 - gi0 >= K.
+__device__ __forceinline__ float bm_group_threshold(const float* __restrict__ grow, int gi0, int gi1,
+                                                    int gc0, int gc1, int K, uint32_t* sbin,
+                                                    uint32_t* s_red, int* s_scan, uint32_t* s_thr,
+                                                    uint32_t& cmax_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g0 = gc0 + tid * kBmGrpPer;
+  float gv[kBmGrpPer];
+#pragma unroll
+  for (int u = 0; u < kBmGrpPer; ++u) gv[u] = g0 + u < gc1 ? grow[g0 + u] : -INFINITY;
+  for (int i = tid; i < kBmBins; i += kTkThreads) sbin[i] = 0;
+  uint32_t in = 0, cmin = 0xFFFFFFFFu, cimax = 0u, cmax = 0u;
+#pragma unroll
+  for (int u = 0; u < kBmGrpPer; ++u) {
+    const int gi = g0 + u;
+    const uint32_t cd = f32_order_key(gv[u]);
+    if (gi < gc1) cmax = cd > cmax ? cd : cmax;
+    if (gi >= gi0 && gi < gi1) {
+      in |= 1u << u;
+      cmin = cd < cmin ? cd : cmin;
+      cimax = cd > cimax ? cd : cimax;
+    }
+  }
+  cmin = wave_minmax_u32<false>(cmin);
+  cimax = wave_minmax_u32<true>(cimax);
+  cmax = wave_minmax_u32<true>(cmax);
+  if (lane == 0) {
+    s_red[wave] = cmin;
+    s_red[kTkWaves + wave] = cimax;
+    s_red[2 * kTkWaves + wave] = cmax;
+  }
+  __syncthreads();
+  cmin = 0xFFFFFFFFu;
+  cimax = 0u;
+  cmax = 0u;
+#pragma unroll
+  for (int w = 0; w < kTkWaves; ++w) {
+    cmin = s_red[w] < cmin ? s_red[w] : cmin;
+    cimax = s_red[kTkWaves + w] > cimax ? s_red[kTkWaves + w] : cimax;
+    cmax = s_red[2 * kTkWaves + w] > cmax ? s_red[2 * kTkWaves + w] : cmax;
+  }
+  cmax_out = cmax;
+  return f32_from_order_key(bm_kth_bin_edge(gv, in, K, cmin, cimax, sbin, s_scan, s_thr));
+}
+
+// The blocks [sb0, sb1) of brow (at most kTkThreads * kBmSegPer) whose
+// maximum reaches thr, in index order, into cb; returns their count.  bv
+// holds this thread's maxima, blocks sb0 + kBmSegPer * tid + u.
+__device__ __forceinline__ int bm_list_blocks(const float (&bv)[kBmSegPer], int sb0, int sb1,
+                                              float thr, int* cb, int* s_scan) {
+  const int tid = threadIdx.x;
+  const int b0 = sb0 + tid * kBmSegPer;
+  uint32_t flags = 0;
+#pragma unroll
+  for (int u = 0; u < kBmSegPer; ++u) flags |= uint32_t(b0 + u < sb1 && bv[u] >= thr) << u;
+  int ncb;
+  int pos = block_scan1<false>(__popc(flags), ncb, s_scan);   // a barrier follows
+  for (uint32_t f = flags; f; f &= f - 1) cb[pos++] = b0 + __ffs(f) - 1;
+  __syncthreads();
+  return ncb;
+}
+
+// GROUPS: the threshold from the group maxima gm (the host has checked
+// that at least K groups lie wholly inside the competition blocks), else
+// from all block maxima.
+template <bool GROUPS>
 __global__ __launch_bounds__(kTkThreads) void topk_bm_seg_kernel(const float* __restrict__ keys,
                                                                  const float* __restrict__ bm,
+                                                                 const float* __restrict__ gm,
                                                                  int n, int nb, int k, int n_sink,
                                                                  int n_local, void* ws) {
   __shared__ __align__(16) uint32_t sbin[kBmBins];
@@ -1510,7 +1635,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_seg_kernel(const float* __
   __shared__ int s_cnt[128];
   __shared__ float ckey[kBmSegCap];
   __shared__ int cidx[kBmSegCap];
-  __shared__ uint32_t s_red[2 * kTkWaves];
+  __shared__ uint32_t s_red[(GROUPS ? 3 : 2) * kTkWaves];
   __shared__ int s_scan[4 * kTkWaves];
   __shared__ uint32_t s_thr;
   __shared__ uint32_t s_h[kBmSegBins];
@@ -1532,19 +1657,40 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_seg_kernel(const float* __
     if (tid == 0) *count = -1;
     return;
   }
+  const float* brow = bm + size_t(row) * nb + blo;
   float thr;
-  int ncb;
   uint32_t cmax;
-  if (!bm_candidate_blocks(bm + size_t(row) * nb + blo, nbc, K, sbin, cb, s_red, s_scan, &s_thr,
-                           thr, ncb, cmax)) {
-    if (tid == 0) *count = -1;
-    return;
+  int nc = 0;
+  if constexpr (GROUPS) {
+    // groups wholly inside the competition blocks, and those meeting them
+    const int gi0 = (blo + kBmGrp - 1) / kBmGrp, gi1 = (blo + nbc) / kBmGrp;
+    const int gc0 = blo / kBmGrp, gc1 = (blo + nbc + kBmGrp - 1) / kBmGrp;
+    // a contiguous eighth of the competition blocks; its maxima are loaded
+    // with the group maxima (one round of loads)
+    const int sb0 = int((long long)nbc * seg / kBmSegs), sb1 = int((long long)nbc * (seg + 1) / kBmSegs);
+    float bv[kBmSegPer];
+#pragma unroll
+    for (int u = 0; u < kBmSegPer; ++u) {
+      const int b = sb0 + tid * kBmSegPer + u;
+      bv[u] = b < sb1 ? brow[b] : -INFINITY;
+    }
+    const int ngr = (nb + kBmGrp - 1) / kBmGrp;
+    thr = bm_group_threshold(gm + size_t(row) * ngr, gi0, gi1, gc0, gc1, K, sbin, s_red, s_scan,
+                             &s_thr, cmax);
+    const int ncb = bm_list_blocks(bv, sb0, sb1, thr, cb, s_scan);
+    if (ncb > 0)
+      nc = bm_collect<4>(keys, base, blo, cb, ncb, thr, ckey, cidx, kBmSegCap, s_cnt, s_scan);
+  } else {
+    int ncb;
+    if (!bm_candidate_blocks(brow, nbc, K, sbin, cb, s_red, s_scan, &s_thr, thr, ncb, cmax)) {
+      if (tid == 0) *count = -1;
+      return;
+    }
+    const int j0 = int((long long)ncb * seg / kBmSegs), j1 = int((long long)ncb * (seg + 1) / kBmSegs);
+    if (j1 > j0)
+      nc = bm_collect<4>(keys, base, blo, cb + j0, j1 - j0, thr, ckey, cidx, kBmSegCap, s_cnt, s_scan);
   }
   const uint32_t tc = s_thr;
-  const int j0 = int((long long)ncb * seg / kBmSegs), j1 = int((long long)ncb * (seg + 1) / kBmSegs);
-  int nc = 0;
-  if (j1 > j0)
-    nc = bm_collect<4>(keys, base, blo, cb + j0, j1 - j0, thr, ckey, cidx, kBmSegCap, s_cnt, s_scan);
   if (nc > kBmSegCap) {
     if (tid == 0) *count = -1;
     return;
@@ -1554,7 +1700,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_seg_kernel(const float* __
     const uint32_t c = f32_order_key(ckey[i]);
     wcode[i] = c;
     widx[i] = cidx[i];
-    atomicAdd(&s_h[(c - tc) >> hsh], 1u);               // tc <= c <= cmax
+    const uint32_t hb = (c - tc) >> hsh;                // tc <= c <= cmax: hb < kBmSegBins
+    atomicAdd(&s_h[hb < kBmSegBins ? hb : kBmSegBins - 1], 1u);
   }
   __syncthreads();
   if (tid < kBmSegBins) whist[tid] = s_h[tid];
@@ -1920,10 +2067,10 @@ extern "C" size_t topk_select_block_max_split_workspace_bytes(int rows, int n) {
   return size_t(rows) * bm_split_ws_per_row();
 }
 
-extern "C" int topk_select_block_max_split(const float* keys, const float* block_max, int rows,
-                                           int n, int k, int n_sink, int n_local,
-                                           int32_t* idx_out, void* ws, size_t ws_bytes,
-                                           hipStream_t stream) {
+extern "C" int topk_select_block_max_split(const float* keys, const float* block_max,
+                                           const float* group_max, int rows, int n, int k,
+                                           int n_sink, int n_local, int32_t* idx_out, void* ws,
+                                           size_t ws_bytes, hipStream_t stream) {
   const char* nm = "topk_select_block_max_split";
   int stride = 0;
   const int rc = topk_validate(nm, keys, SDQ_KEY_F32_MAX, rows, n, k, n_sink, n_local, idx_out,
@@ -1940,8 +2087,17 @@ extern "C" int topk_select_block_max_split(const float* keys, const float* block
               ws_bytes);
   SDQ_REQUIRE(reinterpret_cast<uintptr_t>(ws) % 16 == 0, "%s: ws must be 16-byte aligned", nm);
   if (stride == 0) return SDQ_OK;
-  hipLaunchKernelGGL(topk_bm_seg_kernel, dim3(kBmSegs, rows), dim3(kTkThreads), 0, stream, keys,
-                     block_max, n, n / 64, k, n_sink, n_local, ws);
+  // the group maxima are used when at least K groups lie wholly inside the
+  // competition blocks
+  const int m = n - n_sink - n_local, K = k < m ? k : m;
+  const int blo = n_sink / 64, bhi = (n - n_local) / 64;
+  const bool groups = group_max && (bhi / kBmGrp) - (blo + kBmGrp - 1) / kBmGrp >= K;
+  if (groups)
+    hipLaunchKernelGGL(topk_bm_seg_kernel<true>, dim3(kBmSegs, rows), dim3(kTkThreads), 0, stream,
+                       keys, block_max, group_max, n, n / 64, k, n_sink, n_local, ws);
+  else
+    hipLaunchKernelGGL(topk_bm_seg_kernel<false>, dim3(kBmSegs, rows), dim3(kTkThreads), 0, stream,
+                       keys, block_max, nullptr, n, n / 64, k, n_sink, n_local, ws);
   hipLaunchKernelGGL(topk_bm_final_kernel, dim3(rows), dim3(kTkThreads), 0, stream, keys, n, k,
                      n_sink, n_local, ws, idx_out, stride);
   return check_launch(nm);

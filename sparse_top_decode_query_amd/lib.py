@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libsdq.so")
 
 SDQ_KEY_F32_MAX = 0
 SDQ_KEY_U8_MIN = 1
+GROUP_BLOCKS = 8            # SDQ_GROUP_BLOCKS: 64-token blocks per group maximum
 D = 128
 
 _lib = None
@@ -34,12 +35,12 @@ _SIGS = {
     "fathom_plan": ([_vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp], _c_int),
     "fathom_plan_uniform": ([_vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp], _c_int),
     "fathom_gather": ([_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp], _c_int),
-    "fathom_scan": ([_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp], _c_int),
+    "fathom_scan": ([_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp], _c_int),
     "fathom_plan_scan": ([_vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp,
-                          _vp, _vp, _vp, _vp], _c_int),
+                          _vp, _vp, _vp, _vp, _vp], _c_int),
     "topk_select_block_max": ([_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp], _c_int),
-    "topk_select_block_max_split": ([_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _c_size, _vp],
-                                    _c_int),
+    "topk_select_block_max_split": ([_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _c_size,
+                                     _vp], _c_int),
     "topk_select_block_max_split_workspace_bytes": ([_c_int, _c_int], _c_size),
     "topk_select_workspace_bytes": ([_c_int, _c_int, _c_int, _c_int], _c_size),
     "topk_select": ([_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _c_size, _vp], _c_int),
@@ -245,12 +246,27 @@ def fathom_gather(planes_host, meta_host, depth, planes_dev, meta_dev, n=None, s
                                 _vp(meta_dev.data_ptr()), _stream(stream)), "fathom_gather")
 
 
+def n_groups(n):
+    """Group maxima per row for n tokens (SDQ_GROUP_BLOCKS blocks of 64)."""
+    return (_round64(n) // 64 + GROUP_BLOCKS - 1) // GROUP_BLOCKS
+
+
+def _maxima(block_max, group_max, G, n64):
+    bm = gm = _vp(0)
+    if block_max is not None:
+        bm = _dev(block_max, "block_max", 4, G * (n64 // 64))
+    if group_max is not None:
+        gm = _dev(group_max, "group_max", 4, G * n_groups(n64))
+    return bm, gm
+
+
 def fathom_scan(index, depth, qbar, n, scores=None, block_max=None, planes=None, meta=None,
-                stream=None):
+                stream=None, group_max=None):
     """index: PlaneIndex (``planes``/``meta`` override its HBM buffers, e.g. a
     staging copy filled by fathom_gather); the first n tokens of its rows are
     scored -> scores float32 [G][n64], n64 = n rounded up to 64 (tokens past n
-    score -inf); also fills ``block_max`` float32 [G][n64/64] if given."""
+    score -inf); also fills ``block_max`` float32 [G][n64/64] and
+    ``group_max`` float32 [G][n_groups(n)] if given."""
     G, d = depth.shape
     planes = index.planes if planes is None else planes
     meta = index.meta if meta is None else meta
@@ -259,18 +275,16 @@ def fathom_scan(index, depth, qbar, n, scores=None, block_max=None, planes=None,
     _dev(depth, "depth", 1, G * d)
     _dev(qbar, "qbar", 4, G * d)
     scores = _out(scores, (G, n64), torch.float32, planes.device, "scores", 4)
-    bm = _vp(0)
-    if block_max is not None:
-        bm = _dev(block_max, "block_max", 4, G * (n64 // 64))
+    bm, gm = _maxima(block_max, group_max, G, n64)
     _check(load().fathom_scan(_vp(planes.data_ptr()), _vp(meta.data_ptr()), _vp(depth.data_ptr()),
                               _vp(qbar.data_ptr()), G, d, int(n), n_cap, _vp(scores.data_ptr()), bm,
-                              _stream(stream)), "fathom_scan")
+                              gm, _stream(stream)), "fathom_scan")
     return scores
 
 
 def fathom_plan_scan(index, q, key_var, budget_bits, n, depth=None, qbar=None, scores=None,
                      block_max=None, planes=None, meta=None, uniform_channels=None, stream=None,
-                     write_plan=True):
+                     write_plan=True, group_max=None):
     """fathom_plan (or the uniform plan with ``uniform_channels``) and fathom_scan in one
     launch -> (depth, qbar, scores); depth/qbar are None when ``write_plan`` is False."""
     G, d = key_var.shape
@@ -291,14 +305,13 @@ def fathom_plan_scan(index, q, key_var, budget_bits, n, depth=None, qbar=None, s
         depth = qbar = None
         dp = qp = _vp(0)
     scores = _out(scores, (G, n64), torch.float32, q.device, "scores", 4)
-    bm = _vp(0)
-    if block_max is not None:
-        bm = _dev(block_max, "block_max", 4, G * (n64 // 64))
+    bm, gm = _maxima(block_max, group_max, G, n64)
     uniform = uniform_channels is not None
     budget = int(uniform_channels) if uniform else int(budget_bits)
     _check(load().fathom_plan_scan(_vp(q.data_ptr()), _vp(key_var.data_ptr()), rows // G, budget,
                                    int(uniform), _vp(planes.data_ptr()), _vp(meta.data_ptr()), G, d,
-                                   int(n), n_cap, dp, qp, _vp(scores.data_ptr()), bm, _stream(stream)),
+                                   int(n), n_cap, dp, qp, _vp(scores.data_ptr()), bm, gm,
+                                   _stream(stream)),
            "fathom_plan_scan")
     return depth, qbar, scores
 
@@ -322,19 +335,23 @@ def topk_bm_split_workspace(rows, n, device="cuda"):
 
 
 def topk_select_block_max_split(keys, block_max, k, n_sink=0, n_local=0, idx=None, ws=None,
-                                stream=None):
+                                stream=None, group_max=None):
     """topk_select_block_max with each row's candidate gather spread over
-    several workgroups; ws from topk_bm_split_workspace (allocated here if
-    not given)."""
+    several workgroups; ``group_max`` [rows][n_groups(n)] (as fathom_scan
+    writes it) lets each workgroup read only its share of the block maxima;
+    ws from topk_bm_split_workspace (allocated here if not given)."""
     rows, n = keys.shape
     _dev(keys, "keys", 4, rows * n)
     _dev(block_max, "block_max", 4, rows * (n // 64))
+    gm = _vp(0)
+    if group_max is not None:
+        gm = _dev(group_max, "group_max", 4, rows * n_groups(n))
     idx = _out(idx, (rows, k + n_sink + n_local), torch.int32, keys.device, "idx", 4)
     if ws is None:
         ws = topk_bm_split_workspace(rows, n, keys.device)
     _dev(ws, "ws", 1)
-    _check(load().topk_select_block_max_split(_vp(keys.data_ptr()), _vp(block_max.data_ptr()), rows,
-                                              n, int(k), int(n_sink), int(n_local),
+    _check(load().topk_select_block_max_split(_vp(keys.data_ptr()), _vp(block_max.data_ptr()), gm,
+                                              rows, n, int(k), int(n_sink), int(n_local),
                                               _vp(idx.data_ptr()), _vp(ws.data_ptr()), ws.numel(),
                                               _stream(stream)), "topk_select_block_max_split")
     return idx

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     L = sdq.load()
     for name in _declared():
         assert hasattr(L, name), name
-    assert L.sdq_abi_version() == 2
+    assert L.sdq_abi_version() == 3
 
 
 def test_invalid_arguments_rejected_without_launch():
@@ -39,18 +39,18 @@ def test_invalid_arguments_rejected_without_launch():
     null = ctypes.c_void_p(0)
     s = ctypes.c_void_p(0)
     EINVAL = -1
-    assert L.fathom_scan(null, p, p, p, 8, 128, 4096, 4096, p, null, s) == EINVAL
+    assert L.fathom_scan(null, p, p, p, 8, 128, 4096, 4096, p, null, null, s) == EINVAL
     assert b"null" in L.sdq_last_error()
-    assert L.fathom_scan(p, p, p, p, 8, 128, 4096, 4000, p, null, s) == EINVAL   # n_cap % 64
-    assert L.fathom_scan(p, p, p, p, 8, 128, 4097, 4096, p, null, s) == EINVAL   # n > n_cap
-    assert L.fathom_scan(p, p, p, p, 8, 128, 0, 4096, p, null, s) == EINVAL      # n < 1
-    assert L.fathom_scan(p, p, p, p, 8, 128, 64, 1 << 25, p, null, s) == EINVAL  # n_cap >= 2^25
-    assert L.fathom_scan(p, p, p, p, 8, 64, 4096, 4096, p, null, s) == EINVAL    # d != 128
-    assert L.fathom_scan(p, p, p, p, 8, 128, 4096, 4096, ctypes.c_void_p(0x1004), null, s) == EINVAL  # align
+    assert L.fathom_scan(p, p, p, p, 8, 128, 4096, 4000, p, null, null, s) == EINVAL   # n_cap % 64
+    assert L.fathom_scan(p, p, p, p, 8, 128, 4097, 4096, p, null, null, s) == EINVAL   # n > n_cap
+    assert L.fathom_scan(p, p, p, p, 8, 128, 0, 4096, p, null, null, s) == EINVAL      # n < 1
+    assert L.fathom_scan(p, p, p, p, 8, 128, 64, 1 << 25, p, null, null, s) == EINVAL  # n_cap >= 2^25
+    assert L.fathom_scan(p, p, p, p, 8, 64, 4096, 4096, p, null, null, s) == EINVAL    # d != 128
+    assert L.fathom_scan(p, p, p, p, 8, 128, 4096, 4096, ctypes.c_void_p(0x1004), null, null, s) == EINVAL  # align
     assert L.fathom_plan(p, p, 8, 4, 128, -1, p, p, s) == EINVAL             # negative budget
-    assert L.fathom_plan_scan(p, p, 4, 56, 0, p, p, 8, 128, 4096, 4096, p, null, p, null, s) == EINVAL  # depth only
-    assert L.fathom_plan_scan(p, p, 4, 56, 0, p, p, 8, 128, 4096, 4000, null, null, p, null, s) == EINVAL  # n_cap % 64
-    assert L.fathom_plan_scan(p, p, 4, 129, 1, p, p, 8, 128, 4096, 4096, null, null, p, null, s) == EINVAL  # > d channels
+    assert L.fathom_plan_scan(p, p, 4, 56, 0, p, p, 8, 128, 4096, 4096, p, null, p, null, null, s) == EINVAL  # depth only
+    assert L.fathom_plan_scan(p, p, 4, 56, 0, p, p, 8, 128, 4096, 4000, null, null, p, null, null, s) == EINVAL  # n_cap % 64
+    assert L.fathom_plan_scan(p, p, 4, 129, 1, p, p, 8, 128, 4096, 4096, null, null, p, null, null, s) == EINVAL  # > d channels
     assert L.fathom_plan_uniform(p, p, 8, 4, 128, 129, p, p, s) == EINVAL    # > d channels
     assert L.fathom_ingest(p, 0, 4096, 128, p, p, s) == EINVAL               # G < 1
     assert L.fathom_append(p, 8, 128, 4096, 4000, 97, p, p, s) == EINVAL     # past n_cap
@@ -70,12 +70,12 @@ def test_invalid_arguments_rejected_without_launch():
     assert b"static scratch" in L.sdq_last_error()
     assert L.topk_select_noalloc(p, 7, 1, 10, 2, 0, 0, p, s) == EINVAL             # key type
     ws_bm = L.topk_select_block_max_split_workspace_bytes(8, 1 << 20)
-    assert L.topk_select_block_max_split(p, p, 8, 1 << 20, 512, 0, 0, p, null, ws_bm, s) == EINVAL  # no ws
-    assert L.topk_select_block_max_split(p, p, 8, 1 << 20, 512, 0, 0, p, p, ws_bm - 1, s) == EINVAL  # short
+    assert L.topk_select_block_max_split(p, p, null, 8, 1 << 20, 512, 0, 0, p, null, ws_bm, s) == EINVAL  # no ws
+    assert L.topk_select_block_max_split(p, p, null, 8, 1 << 20, 512, 0, 0, p, p, ws_bm - 1, s) == EINVAL  # short
     assert b"workspace" in L.sdq_last_error()
-    assert L.topk_select_block_max_split(p, null, 8, 1 << 20, 512, 0, 0, p, p, ws_bm, s) == EINVAL  # bm
-    assert L.topk_select_block_max_split(p, p, 8, 1000, 512, 0, 0, p, p, ws_bm, s) == EINVAL  # n % 64
-    assert L.topk_select_block_max_split(p, p, 8, 1 << 21, 512, 0, 0, p, p, 1 << 30, s) == EINVAL  # > 2^20
+    assert L.topk_select_block_max_split(p, null, null, 8, 1 << 20, 512, 0, 0, p, p, ws_bm, s) == EINVAL  # bm
+    assert L.topk_select_block_max_split(p, p, null, 8, 1000, 512, 0, 0, p, p, ws_bm, s) == EINVAL  # n % 64
+    assert L.topk_select_block_max_split(p, p, null, 8, 1 << 21, 512, 0, 0, p, p, 1 << 30, s) == EINVAL  # > 2^20
     assert L.hamming_scan(p, p, 0, 10, 10, p, s) == EINVAL
     assert L.hamming_scan(p, p, 4, 11, 10, p, s) == EINVAL                   # n > n_cap
     assert L.hamming_scan_topk(p, p, 4, 11, 10, 2, 0, 0, p, p, p, 256, s) == EINVAL   # n > n_cap

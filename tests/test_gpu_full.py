@@ -106,18 +106,21 @@ def test_ingest_1m_bitexact(layer):
 @pytest.mark.parametrize("budget,uniform", PLANS, ids=["B47", "B56", "B92", "uniform34x4"])
 def test_fused_plan_scan_1m_all_heads(layer, budget, uniform):
     """The decode step's own launches at full size: fused plan + scan with
-    block maxima, block-max top-k, gather attention.  Plans bit-exact; every
-    score of all 8 rows within 1e-3 of the row's range; block maxima exact on
-    the GPU's scores; top-k exact on the GPU's scores and equal to the
+    block and group maxima, block-max top-k, gather attention.  Plans
+    bit-exact; every score of all 8 rows within 1e-3 of the row's range; block
+    and group maxima exact on the GPU's scores; top-k exact on the GPU's
+    scores and equal to the
     oracle's set up to near-tie swaps; the planted needles selected;
     attention of all 32 query heads within 2e-2 of float64."""
     lib, case, G, n, k = layer["lib"], layer["case"], layer["G"], layer["n"], layer["case"]["k"]
     _say(f"fused plan + scan n=2^20 G=8 budget={budget} uniform={uniform}")
     bm = torch.empty(G, n // 64, device="cuda")
+    gm = torch.empty(G, lib.n_groups(n), device="cuda")
     depth, qbar, scores = lib.fathom_plan_scan(layer["index"], layer["q"], layer["var"], budget, n,
-                                               block_max=bm, uniform_channels=uniform)
-    idx = lib.topk_select_block_max_split(scores, bm, k)
+                                               block_max=bm, uniform_channels=uniform, group_max=gm)
+    idx = lib.topk_select_block_max_split(scores, bm, k, group_max=gm)
     assert torch.equal(idx, lib.topk_select_block_max(scores, bm, k))
+    assert torch.equal(idx, lib.topk_select_block_max_split(scores, bm, k))
     out = lib.gather_attend(layer["q"].view(1, G * 4, 128), layer["K"].view(1, G, n, 128),
                             layer["V"].view(1, G, n, 128), idx.view(1, G, k))
     # the two-call form (plan, then scan) gives the identical scores
@@ -131,6 +134,7 @@ def test_fused_plan_scan_1m_all_heads(layer, budget, uniform):
     S = host(scores)
     _assert_rows(S, ref)
     assert np.array_equal(host(bm), S.reshape(G, n // 64, 64).max(axis=2))
+    assert np.array_equal(host(gm), S.reshape(G, n // 512, 512).max(axis=2))
     I = host(idx)
     for g in range(G):
         tol = SCORE_RTOL * float(ref[g].max() - ref[g].min())

@@ -61,17 +61,19 @@ def test_fathom_step_graph_replay(sdq):
     index = sdq.fathom_ingest(K)
     scores = torch.empty(G, n, device="cuda")
     bm = torch.empty(G, n // 64, device="cuda")
+    gm = torch.empty(G, sdq.n_groups(n), device="cuda")
     idx = torch.empty(G, k, dtype=torch.int32, device="cuda")
     out = torch.empty(1, G * 4, 128, device="cuda")
     ws = sdq.attend_workspace(1, G * 4, G, False, k, 1)
     ws_bm = sdq.topk_bm_split_workspace(G, n)
 
     def step():
-        sdq.fathom_plan_scan(index, q, var, 56, n, scores=scores, block_max=bm, write_plan=False)
-        sdq.topk_select_block_max_split(scores, bm, k, idx=idx, ws=ws_bm)
+        sdq.fathom_plan_scan(index, q, var, 56, n, scores=scores, block_max=bm, write_plan=False,
+                             group_max=gm)
+        sdq.topk_select_block_max_split(scores, bm, k, idx=idx, ws=ws_bm, group_max=gm)
         sdq.gather_attend(q.view(1, G * 4, 128), K.view(1, G, n, 128), V.view(1, G, n, 128),
                           idx.view(1, G, k), out=out, ws=ws)
-    _check_replays(step, [scores, bm, idx, out])
+    _check_replays(step, [scores, bm, gm, idx, out])
 
 
 def test_hamming_step_graph_replay(sdq):

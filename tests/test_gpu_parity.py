@@ -16,6 +16,7 @@ from oracle import fathom as o_fathom
 from oracle import hamming as o_hamming
 from oracle import quest as o_quest
 from oracle import select as o_select
+from sparse_top_decode_query_amd import lib as sdq_lib
 
 pytestmark = pytest.mark.gpu
 
@@ -49,6 +50,17 @@ def dev(a):
 def host(t, dtype=None):
     x = t.cpu().numpy()
     return x.view(dtype) if dtype is not None else x
+
+
+def _groups_of(bm):
+    """Group maxima (sdq.GROUP_BLOCKS blocks a group, the last one shorter)
+    of block maxima [rows][nb], as plain torch ops."""
+    rows, nb = bm.shape
+    gb = sdq_lib.GROUP_BLOCKS
+    ng = (nb + gb - 1) // gb
+    pad = torch.full((rows, ng * gb), float("-inf"), device=bm.device)
+    pad[:, :nb] = bm
+    return pad.view(rows, ng, gb).amax(-1)
 
 
 def _assert_scores(gpu, ref):
@@ -229,10 +241,12 @@ def _scan_case(sdq, G, n, budget, uniform=None):
     index = sdq.fathom_ingest(dev(case["K"]))
     depth, qbar = sdq.fathom_plan(dev(q), dev(var), budget, uniform_channels=uniform)
     bm = torch.empty(G, n // 64, device="cuda")
-    scores = sdq.fathom_scan(index, depth, qbar, n, block_max=bm)
+    gm = torch.empty(G, sdq.n_groups(n), device="cuda")
+    scores = sdq.fathom_scan(index, depth, qbar, n, block_max=bm, group_max=gm)
     torch.cuda.synchronize()
-    # block maxima are exactly the maxima of the written scores
+    # block and group maxima are exactly the maxima of the written scores
     assert torch.equal(bm, scores.view(G, n // 64, 64).amax(-1))
+    assert torch.equal(gm, _groups_of(bm))
     rp, rm = o_fathom.ingest(case["K"])
     rd, rq = o_fathom.plan_heads(q, var, 4, budget=budget, n_uniform=uniform)
     ref = o_fathom.scan_heads(rp, rm, rd, rq, n)
@@ -269,13 +283,16 @@ def test_fathom_plan_scan_fused_equals_separate(sdq, G, n, budget, uniform):
     bm = torch.empty(G, n // 64, device="cuda")
     scores = sdq.fathom_scan(index, depth, qbar, n, block_max=bm)
     bm2 = torch.full((G, n // 64), 7.0, device="cuda")
-    d2, q2, s2 = sdq.fathom_plan_scan(index, q, var, budget, n, block_max=bm2, uniform_channels=uniform)
+    gm2 = torch.full((G, sdq.n_groups(n)), 7.0, device="cuda")
+    d2, q2, s2 = sdq.fathom_plan_scan(index, q, var, budget, n, block_max=bm2, uniform_channels=uniform,
+                                      group_max=gm2)
     _, _, s3 = sdq.fathom_plan_scan(index, q, var, budget, n, uniform_channels=uniform, write_plan=False)
     torch.cuda.synchronize()
     assert torch.equal(d2, depth) and torch.equal(q2.view(torch.int32), qbar.view(torch.int32))
     assert torch.equal(s2.view(torch.int32), scores.view(torch.int32))
     assert torch.equal(s3.view(torch.int32), scores.view(torch.int32))
     assert torch.equal(bm2.view(torch.int32), bm.view(torch.int32))
+    assert torch.equal(gm2, _groups_of(bm))
 
 
 # ---------------------------------------------------------------- top-k
@@ -336,7 +353,12 @@ def test_topk_f32_degenerate_rows(sdq):
 
 
 @pytest.mark.parametrize("rows,n,k,ns,nl", [(8, 1 << 20, 512, 0, 0), (2, 65536 + 128, 64, 64, 64),
-                                            (3, 100032, 1563, 0, 0), (1, 131072, 4096, 0, 0)])
+                                            (3, 100032, 1563, 0, 0), (1, 131072, 4096, 0, 0),
+                                            # windows and lengths that cut groups; a K just
+                                            # within / beyond the whole groups (group path /
+                                            # all block maxima)
+                                            (2, 1 << 20, 512, 192, 64 * 21), (3, 64 * 4099, 300, 64, 0),
+                                            (2, 64 * 800, 97, 64 * 7, 64 * 9), (2, 64 * 800, 99, 64, 64)])
 def test_topk_block_max_bitexact(sdq, rows, n, k, ns, nl):
     _say(f"topk block-max rows={rows} n={n} k={k}")
     g = np.random.default_rng(n + 3 * k)
@@ -344,9 +366,11 @@ def test_topk_block_max_bitexact(sdq, rows, n, k, ns, nl):
     keys[:, ::5] = np.round(keys[:, ::5], 1)
     kt = dev(keys)
     bm = kt.view(rows, n // 64, 64).amax(-1).contiguous()
+    gm = _groups_of(bm)
     ref = _topk_ref(keys, k, ns, nl, True)
     assert np.array_equal(host(sdq.topk_select_block_max(kt, bm, k, ns, nl)), ref)
     assert np.array_equal(host(sdq.topk_select_block_max_split(kt, bm, k, ns, nl)), ref)
+    assert np.array_equal(host(sdq.topk_select_block_max_split(kt, bm, k, ns, nl, group_max=gm)), ref)
     assert np.array_equal(host(sdq.topk_select(kt, k, ns, nl)), ref)
 
 
@@ -360,11 +384,35 @@ def test_topk_block_max_degenerate(sdq):
     keys[2, 64 * 100:64 * 164] = np.arange(64 * 64, dtype=np.float32)   # top keys in 64 blocks
     kt = dev(keys)
     bm = kt.view(3, n // 64, 64).amax(-1).contiguous()
+    gm = _groups_of(bm)
     for k in (1, 512, 2048):
         ref = _topk_ref(keys, k, 0, 0, True)
         assert np.array_equal(host(sdq.topk_select_block_max(kt, bm, k)), ref), k
         assert np.array_equal(host(sdq.topk_select_block_max_split(kt, bm, k)), ref), k
+        assert np.array_equal(host(sdq.topk_select_block_max_split(kt, bm, k, group_max=gm)), ref), k
         assert np.array_equal(host(sdq.topk_select(kt, k)), ref), k
+
+
+def test_topk_block_max_split_workspace_reuse(sdq):
+    """Calls in a row on one split workspace, fewer rows than it was sized
+    for, rows that take the exact row path in between: every call is exact
+    whatever the last call left in the workspace."""
+    _say("topk block-max split workspace reuse")
+    g = np.random.default_rng(404)
+    n = 1 << 17
+    ws = sdq.topk_bm_split_workspace(6, n)
+    for rows, k, tied in ((6, 512, False), (2, 300, True), (5, 1, False), (1, 2048, True),
+                          (6, 700, False), (3, 64, False)):
+        keys = (g.standard_normal((rows, n)) * 2).astype(np.float32)
+        if tied:
+            keys[0] = 0.5                            # every block ties: row path
+        kt = dev(keys)
+        bm = kt.view(rows, n // 64, 64).amax(-1).contiguous()
+        ref = _topk_ref(keys, k, 0, 0, True)
+        got = host(sdq.topk_select_block_max_split(kt, bm, k, ws=ws))
+        assert np.array_equal(got, ref), (rows, k, tied)
+        got = host(sdq.topk_select_block_max_split(kt, bm, k, ws=ws, group_max=_groups_of(bm)))
+        assert np.array_equal(got, ref), (rows, k, tied, "groups")
 
 
 @pytest.mark.parametrize("rows,n,k,ns,nl,dist", [(32, 131072, 512, 128, 128, "binom"),
