@@ -368,7 +368,7 @@ int minmax_block_scan(const uint16_t* bmin, const uint16_t* bmax, const float* q
  *         holds the partial results of sets split over several workgroups;
  *         its contents on entry do not matter.  Calls sharing a workspace
  *         must not overlap.
- * K and V must be 16-byte aligned; n < 2^23 (byte offsets within one
+ * q, K and V must be 16-byte aligned; n < 2^23 (byte offsets within one
  * (request, KV head) slice fit 31 bits); H_q / H_kv in {1, 2, 4, 8} when sets
  * are shared; R * H_sel <= 65535.
  * Errors: SDQ_EINVAL on null pointers, R, H_q, H_kv, n, n_idx, block_tokens

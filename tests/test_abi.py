@@ -88,6 +88,9 @@ def test_invalid_arguments_rejected_without_launch():
     assert L.gather_attend(p, p, p, p, 1, 32, 8, 0, 1 << 23, 1 << 23, 512, 1, 128, 1.0, p, p, 1 << 20,
                            s) == EINVAL
     assert L.gather_attend(p, p, p, p, 1, 32, 8, 0, 2001, 2000, 8, 1, 128, 1.0, p, p, 1 << 20, s) == EINVAL
+    assert L.gather_attend(ctypes.c_void_p(0x1004), p, p, p, 1, 32, 8, 0, 2000, 2000, 8, 1, 128, 1.0, p, p,
+                           1 << 20, s) == EINVAL                                 # q misaligned
+    assert b"aligned" in L.sdq_last_error()
     assert L.oasis_select(p, 1025, p, 64, 4, p, p, 16, 0, 2, p, p, p, null, s) == EINVAL    # K
     assert L.oasis_select(p, 16, p, 64, 4, p, p, 0, 0, 2, p, p, p, null, s) == EINVAL       # S
     assert L.oasis_select(p, 16, p, 70000, 4, p, p, 16, 0, 2, p, p, p, null, s) == EINVAL   # nb
