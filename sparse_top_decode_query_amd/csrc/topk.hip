@@ -1552,6 +1552,24 @@ __device__ __forceinline__ int bm_seg_bin_shift(uint32_t lo, uint32_t hi) {
   return w > 8 ? w - 8 : 0;
 }
 
+// v = p[i0 .. i0 + 4), entries at or past `end` read as -inf: one 16-byte load
+// when all four are in range and p + i0 is 16-byte aligned (single loads
+// with a 16-byte stride between lanes would pass four times the addresses
+// through the CU's address unit).
+__device__ __forceinline__ void load4_or_neg_inf(const float* __restrict__ p, int i0, int end,
+                                                 float (&v)[4]) {
+  if (i0 + 4 <= end && (reinterpret_cast<uintptr_t>(p + i0) & 15) == 0) {
+    const float4 x = *reinterpret_cast<const float4*>(p + i0);
+    v[0] = x.x;
+    v[1] = x.y;
+    v[2] = x.z;
+    v[3] = x.w;
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = i0 + u < end ? p[i0 + u] : -INFINITY;
+  }
+}
+
 // Threshold from the group maxima (all threads of the workgroup call it).
 // Groups [gi0, gi1) lie wholly inside the competition blocks: the K-th
 // largest of their maxima, T', is <= the K-th largest block maximum T (the K
@@ -1567,8 +1585,7 @@ __device__ __forceinline__ float bm_group_threshold(const float* __restrict__ gr
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g0 = gc0 + tid * kBmGrpPer;
   float gv[kBmGrpPer];
-#pragma unroll
-  for (int u = 0; u < kBmGrpPer; ++u) gv[u] = g0 + u < gc1 ? grow[g0 + u] : -INFINITY;
+  load4_or_neg_inf(grow, g0, gc1, gv);
   for (int i = tid; i < kBmBins; i += kTkThreads) sbin[i] = 0;
   uint32_t in = 0, cmin = 0xFFFFFFFFu, cimax = 0u, cmax = 0u;
 #pragma unroll
@@ -1669,11 +1686,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_seg_kernel(const float* __
     // with the group maxima (one round of loads)
     const int sb0 = int((long long)nbc * seg / kBmSegs), sb1 = int((long long)nbc * (seg + 1) / kBmSegs);
     float bv[kBmSegPer];
-#pragma unroll
-    for (int u = 0; u < kBmSegPer; ++u) {
-      const int b = sb0 + tid * kBmSegPer + u;
-      bv[u] = b < sb1 ? brow[b] : -INFINITY;
-    }
+    load4_or_neg_inf(brow, sb0 + tid * kBmSegPer, sb1, bv);
     const int ngr = (nb + kBmGrp - 1) / kBmGrp;
     thr = bm_group_threshold(gm + size_t(row) * ngr, gi0, gi1, gc0, gc1, K, sbin, s_red, s_scan,
                              &s_thr, cmax);
