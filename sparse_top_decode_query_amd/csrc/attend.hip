@@ -136,18 +136,25 @@ __global__ __launch_bounds__(kAtThreads) void attend_kernel(AttendArgs a) {
   AtState<NQ> st;
   at_init(st);
 
-  // two register buffers: the next slab is requested before the current one
-  // is used; slabs past the wave's last are not requested at all (a skipped
-  // row's load reads no memory, but its addresses still pass through the
-  // CU's address unit)
-  if (my_slabs > 0) {
+  // A wave with one slab requests it and works on it.  With more, two
+  // register buffers: the next slab is requested before the current one is
+  // used, in straight-line turns (slabs past the wave's last read as skipped
+  // rows: no memory access, though their addresses still pass through the
+  // CU's address unit; branching around them instead cost the long-set case
+  // 3 % through the schedule of the loop).
+  if (my_slabs == 1) {
+    u32x4_t kA[kAtGroups][4], vA[kAtGroups][4];
+    uint32_t mA;
+    fetch(0, kA, vA, mA);
+    at_compute<NQ>(st, qf, kA, vA, mA, a.scale_log2);
+  } else if (my_slabs > 1) {
     u32x4_t kA[kAtGroups][4], vA[kAtGroups][4], kB[kAtGroups][4], vB[kAtGroups][4];
     uint32_t mA, mB;
     fetch(0, kA, vA, mA);
     for (int s = 0; s < my_slabs; s += 2) {
-      if (s + 1 < my_slabs) fetch(s + 1, kB, vB, mB);
+      fetch(s + 1, kB, vB, mB);
       at_compute<NQ>(st, qf, kA, vA, mA, a.scale_log2);
-      if (s + 2 < my_slabs) fetch(s + 2, kA, vA, mA);
+      fetch(s + 2, kA, vA, mA);
       if (s + 1 < my_slabs) at_compute<NQ>(st, qf, kB, vB, mB, a.scale_log2);
     }
   }
