@@ -403,6 +403,13 @@ def main():
         "fixed_cost": "the same launch with budget 0 over 64 tokens per KV head (dispatch, plan, drain)",
         "frac_excluding_fixed_cost": round(scan_bytes / ((scan_launch_us - scan_fixed_us) * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
     }
+    # the published peak is the roofline's; beside it, what plain streaming
+    # kernels reach on this machine
+    hbm_meas = hbm_microbench(torch, dev)
+    roofline["measured_hbm"] = hbm_meas
+    # the scan reads and writes (76 MB read, 34 MB of scores written at
+    # B = 56), a mix closest to a copy's
+    roofline["frac_of_measured_copy"] = round(achieved_gbs / hbm_meas["copy_GBps"], 4)
     roofline_valu = {
         "bound": "alu", "achieved": round(scan_ops / scan_s / 1e12, 3),
         "peak": round(VALU_PEAK_OPS / 1e12, 1), "unit": "Tops/s (plane-bit accumulates)",
@@ -966,6 +973,42 @@ def variant_minmax(torch, np, lib, bytemodel, synth, dev, timeit):
             "attend_hbm_frac": round(ab / (us["attend"] * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
             "launch_timing": "back-to-back calls (a replayed HIP graph) over 2 summary copies"}
     return us_step, us["scan"], info
+
+
+def hbm_microbench(torch, dev, nbytes=1 << 30, reps=10):
+    """HBM rates of plain streaming kernels on this machine: a full reduction
+    (read), a device copy (read + write) and a fill (write) over 1 GiB
+    buffers, two of each alternating (2 GiB, far past the 256 MB last-level
+    cache), launched back to back between two events.  The roofline's peak stays the
+    published 8 TB/s; these say how much of it a kernel can reach here."""
+    n = nbytes // 4
+    a = [torch.ones(n, dtype=torch.float32, device=dev) for _ in range(2)]
+    b = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(2)]
+    out = torch.empty((), dtype=torch.float32, device=dev)
+
+    def eager(fn):
+        # each call is hundreds of microseconds of GPU work, far above its
+        # host-side launch cost, so eager launches run back to back (a
+        # reduction is not captured into a graph here: it may record memsets)
+        for i in range(2):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    read = eager(lambda i: torch.sum(a[i % 2], dim=0, out=out))
+    copy = eager(lambda i: b[i % 2].copy_(a[i % 2]))
+    write = eager(lambda i: b[i % 2].zero_())
+    del a, b
+    return {"read_GBps": round(nbytes / (read * 1e-6) / 1e9, 1),
+            "copy_GBps": round(2 * nbytes / (copy * 1e-6) / 1e9, 1),
+            "write_GBps": round(nbytes / (write * 1e-6) / 1e9, 1),
+            "bytes": nbytes, "kernels": "torch sum (read), copy_ (read + write), zero_ (write)"}
 
 
 def copy_calibration(torch, dev):
