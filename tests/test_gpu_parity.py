@@ -393,6 +393,38 @@ def test_topk_block_max_degenerate(sdq):
         assert np.array_equal(host(sdq.topk_select(kt, k)), ref), k
 
 
+def test_topk_block_max_split_groups_randomized(sdq):
+    """Seeded random shapes for the split form with group maxima: lengths that
+    cut groups, windows of any multiple of 64, k from 1 to the block count,
+    and keys that are plain, heavily tied, or with the winners packed into
+    one stretch of the row (which overflows a segment's share or needs many
+    blocks of one group) -- each against the oracle."""
+    _say("topk block-max split groups randomized")
+    g = np.random.default_rng(2024)
+    for case in range(12):
+        rows = int(g.integers(1, 4))
+        nb = int(g.integers(24, 4097))
+        n = 64 * nb
+        ns = 64 * int(g.integers(0, max(1, nb // 8)))
+        nl = 64 * int(g.integers(0, max(1, nb // 8)))
+        nbc = nb - ns // 64 - nl // 64
+        k = int(g.integers(1, nbc + 1))
+        keys = (g.standard_normal((rows, n)) * 2).astype(np.float32)
+        kind = case % 3
+        if kind == 1:
+            keys = np.round(keys, 0).astype(np.float32)             # heavy ties
+        elif kind == 2:
+            a = int(g.integers(0, max(1, n - 8 * k)))
+            keys[:, a:a + 4 * k] += 10.0                             # winners in one stretch
+        kt = dev(keys)
+        bm = kt.view(rows, nb, 64).amax(-1).contiguous()
+        ref = _topk_ref(keys, k, ns, nl, True)
+        got = host(sdq.topk_select_block_max_split(kt, bm, k, ns, nl, group_max=_groups_of(bm)))
+        assert np.array_equal(got, ref), (case, rows, n, k, ns, nl, kind)
+        got = host(sdq.topk_select_block_max_split(kt, bm, k, ns, nl))
+        assert np.array_equal(got, ref), (case, rows, n, k, ns, nl, kind, "no groups")
+
+
 def test_topk_block_max_split_workspace_reuse(sdq):
     """Calls in a row on one split workspace, fewer rows than it was sized
     for, rows that take the exact row path in between: every call is exact
