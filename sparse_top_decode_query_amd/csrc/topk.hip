@@ -193,20 +193,6 @@ __device__ KthResult select_kth(int count, int K, Fetch fetch, uint32_t* hist, u
   return select_kth_in(count, K, fetch, hist, lo, hi);
 }
 
-// Reserves one slot per lane with pred set, one LDS atomic per wave.  The
-// slots of a wave are consecutive in lane order.
-__device__ __forceinline__ int wave_append(bool pred, int* counter) {
-  const uint64_t mask = __ballot(pred);
-  if (!mask) return -1;
-  const int lane = threadIdx.x & 63;
-  const int leader = __ffsll((unsigned long long)mask) - 1;
-  int base = 0;
-  if (lane == leader) base = atomicAdd(counter, __popcll(mask));
-  base = __shfl(base, leader, 64);
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  return pred ? base + __popcll(mask & lt) : -1;
-}
-
 // Writes the fixed positions and padding of one output row.
 __device__ __forceinline__ void write_fixed(int32_t* o, int n, int n_sink, int n_local, int K,
                                             int stride) {
