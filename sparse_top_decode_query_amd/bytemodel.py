@@ -28,11 +28,6 @@ def uniform_index_bytes(tokens: int, layers: int, kv_heads: int, bits_per_token:
     return tokens * layers * kv_heads * bits_per_token // 8
 
 
-def winner_bytes(k: int, sets: int, head_dim: int = 128, elem_bytes: int = 2) -> int:
-    """bf16 K and V rows of k winners for ``sets`` independent selections."""
-    return k * sets * 2 * head_dim * elem_bytes
-
-
 def plane_scan_read_bytes(n: int, depths) -> int:
     """Bytes the plane-prefix scan reads for one decode step of one layer.
 
