@@ -1515,9 +1515,10 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_kernel(const float* __rest
 // candidate block list from all block maxima (phases 1-3) and takes a
 // contiguous share of the list.  Any threshold <= the K-th largest key is
 // exact here: the final selection is exact over whatever the segments keep.
-// Each segment also leaves a 256-bin histogram of its candidates' codes over
-// [code(thr), code of the row's largest key], a range every segment knows, so
-// the final kernel starts its exact search inside the bin of the K-th key.
+// Each segment also leaves a 256-bin histogram of its candidates' code
+// offsets above code(thr), a base every segment knows (bins finer near it,
+// bm_seg_bin), so the final kernel starts its exact search inside the bin of
+// the K-th key, cut at the code of the row's largest key.
 // Workspace per row: a 64-byte header (the segments' counts, then the two
 // range codes), the segments' codes, their indices, their histograms.
 constexpr int kBmSegs = 8;
@@ -1532,11 +1533,24 @@ __host__ __device__ inline size_t bm_split_ws_per_row() {
   return 64 + size_t(kBmSegs) * (kBmSegCap * 8 + kBmSegBins * 4);
 }
 
-// bins of width 2^sh over [lo, hi]: (hi - lo) >> sh < kBmSegBins
-__device__ __forceinline__ int bm_seg_bin_shift(uint32_t lo, uint32_t hi) {
-  const int w = 32 - __clz(hi - lo);
-  return w > 8 ? w - 8 : 0;
+// Segment histogram bins over the offset d = code - code(thr), finer near
+// the threshold, where the K-th key lies (most candidates sit just above
+// it): offsets below 8 take a bin each, and above that every octave
+// [2^e, 2^(e+1)) splits into 8 bins of width 2^(e-3).  Bin order is offset
+// order; bins 0..239 cover every 32-bit offset.
+__device__ __forceinline__ uint32_t bm_seg_bin(uint32_t d) {
+  const int e = 31 - __clz(d | 8u);                    // 3..31
+  const uint32_t b = uint32_t(8 * (e - 2)) + ((d >> (e - 3)) & 7u);
+  return d < 8 ? d : b;
 }
+
+// first offset of bin b, and its width less one
+__device__ __forceinline__ void bm_seg_bin_range(uint32_t b, uint32_t& off, uint32_t& span) {
+  const int s = int(b >> 3) - 1;                        // e - 3
+  off = b < 8 ? b : (8u + (b & 7u)) << s;
+  span = b < 8 ? 0u : (1u << s) - 1u;
+}
+static_assert(8 * 29 + 7 < kBmSegBins, "offset bins fit the segment histogram");
 
 // v = p[i0 .. i0 + 4), entries at or past `end` read as -inf: one 16-byte load
 // when all four are in range and p + i0 is 16-byte aligned (single loads
@@ -1642,7 +1656,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_seg_kernel(const float* __
   __shared__ int s_scan[4 * kTkWaves];
   __shared__ uint32_t s_thr;
   __shared__ uint32_t s_h[kBmSegBins];
-  const int seg = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
+  const int seg = blockIdx.y, row = blockIdx.x, tid = threadIdx.x;
   char* wr = reinterpret_cast<char*>(ws) + size_t(row) * bm_split_ws_per_row();
   int* count = reinterpret_cast<int*>(wr) + seg;
   uint32_t* wcode = reinterpret_cast<uint32_t*>(wr + 64) + size_t(seg) * kBmSegCap;
@@ -1694,13 +1708,11 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_seg_kernel(const float* __
     if (tid == 0) *count = -1;
     return;
   }
-  const int hsh = bm_seg_bin_shift(tc, cmax);
   for (int i = tid; i < nc; i += kTkThreads) {
     const uint32_t c = f32_order_key(ckey[i]);
     wcode[i] = c;
     widx[i] = cidx[i];
-    const uint32_t hb = (c - tc) >> hsh;                // tc <= c <= cmax: hb < kBmSegBins
-    atomicAdd(&s_h[hb < kBmSegBins ? hb : kBmSegBins - 1], 1u);
+    atomicAdd(&s_h[bm_seg_bin(c - tc)], 1u);             // c >= tc: every candidate reaches thr
   }
   __syncthreads();
   if (tid < kBmSegBins) whist[tid] = s_h[tid];
@@ -1799,9 +1811,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_bm_final_kernel(const float* 
     }
   }
   __syncthreads();
-  const int hsh = bm_seg_bin_shift(tc, cmax);
-  const uint32_t blo = tc + (uint32_t(s_bin) << hsh);
-  const uint32_t span = hsh >= 32 ? 0xFFFFFFFFu : ((1u << hsh) - 1u);
+  uint32_t boff, span;
+  bm_seg_bin_range(uint32_t(s_bin), boff, span);
+  const uint32_t blo = tc + boff;                       // <= cmax: the bin holds a candidate
   const uint32_t bhi = cmax - blo > span ? blo + span : cmax;
   const KthResult kr = select_kth_in(
       nc, s_need,
@@ -2091,11 +2103,15 @@ extern "C" int topk_select_block_max_split(const float* keys, const float* block
   const int m = n - n_sink - n_local, K = k < m ? k : m;
   const int blo = n_sink / 64, bhi = (n - n_local) / 64;
   const bool groups = group_max && (bhi / kBmGrp) - (blo + kBmGrp - 1) / kBmGrp >= K;
+  // grid (rows, segments): workgroups go round-robin over the XCDs by linear
+  // id, so with rows a multiple of 8 the segments of row r share XCD r mod 8
+  // with the final kernel's workgroup r, and the workspace they leave it
+  // (and the row's maxima they all read) stays in that XCD's L2
   if (groups)
-    hipLaunchKernelGGL(topk_bm_seg_kernel<true>, dim3(kBmSegs, rows), dim3(kTkThreads), 0, stream,
+    hipLaunchKernelGGL(topk_bm_seg_kernel<true>, dim3(rows, kBmSegs), dim3(kTkThreads), 0, stream,
                        keys, block_max, group_max, n, n / 64, k, n_sink, n_local, ws);
   else
-    hipLaunchKernelGGL(topk_bm_seg_kernel<false>, dim3(kBmSegs, rows), dim3(kTkThreads), 0, stream,
+    hipLaunchKernelGGL(topk_bm_seg_kernel<false>, dim3(rows, kBmSegs), dim3(kTkThreads), 0, stream,
                        keys, block_max, nullptr, n, n / 64, k, n_sink, n_local, ws);
   hipLaunchKernelGGL(topk_bm_final_kernel, dim3(rows), dim3(kTkThreads), 0, stream, keys, n, k,
                      n_sink, n_local, ws, idx_out, stride);
