@@ -28,9 +28,11 @@ struct AttendArgs {
 
 // Merges the nsplit partials of one query head (dim dd) in one pass with a
 // running maximum, kCb partials at a time with each batch's loads issued
-// together (one memory round trip per batch).
+// together (one memory round trip per batch; the launch picks the smallest
+// kCb of 4, 8 and 16 that covers nsplit, or 16, so a short merge issues no
+// padding loads).
+template <int kCb>
 __device__ float merge_splits(const float* __restrict__ base, int nsplit, int dd) {
-  constexpr int kCb = 16;
   const size_t pf = attend_partial_floats(kHeadDim);
   float M = kNegBig, L = 0.0f, acc = 0.0f;
   for (int c0 = 0; c0 < nsplit; c0 += kCb) {
@@ -60,12 +62,13 @@ __device__ float merge_splits(const float* __restrict__ base, int nsplit, int dd
 }
 
 // One workgroup per query head of a split call: merges its partials.
+template <int CB>
 __global__ __launch_bounds__(kHeadDim) void attend_combine_kernel(const float* __restrict__ parts,
                                                                   int nsplit,
                                                                   float* __restrict__ out) {
   const int qh = blockIdx.x, dd = threadIdx.x;
   out[size_t(qh) * kHeadDim + dd] =
-      merge_splits(parts + size_t(qh) * nsplit * attend_partial_floats(kHeadDim), nsplit, dd);
+      merge_splits<CB>(parts + size_t(qh) * nsplit * attend_partial_floats(kHeadDim), nsplit, dd);
 }
 
 template <int NQ, bool POW2>
@@ -311,7 +314,10 @@ static int attend_impl(const char* nm, const float* q, const uint16_t* K, const 
     default: launch_attend<8>(grid, pow2, a, stream); break;
   }
   if (nsplit > 1)
-    hipLaunchKernelGGL(attend_combine_kernel, dim3(R * H_q), dim3(kHeadDim), 0, stream,
+    hipLaunchKernelGGL(nsplit <= 4   ? attend_combine_kernel<4>
+                       : nsplit <= 8 ? attend_combine_kernel<8>
+                                     : attend_combine_kernel<16>,
+                       dim3(R * H_q), dim3(kHeadDim), 0, stream,
                        reinterpret_cast<const float*>(ws), int(nsplit), out);
   return check_launch(nm);
 }
