@@ -425,6 +425,33 @@ def test_topk_block_max_split_groups_randomized(sdq):
         assert np.array_equal(got, ref), (case, rows, n, k, ns, nl, kind, "no groups")
 
 
+def test_topk_block_max_split_wide_code_offsets(sdq):
+    """The extremes of the segments' offset histograms (code offsets above
+    code(thr)).  Row 0: the winners are packed into fewer than K blocks of a
+    row of negative keys, so thr is far below zero while the K-th key is
+    positive, more than 2^31 codes above it (the top bins).  Row 1: every key
+    of the row is a distinct float one ulp from the next, shuffled, so the
+    K-th key lies a few hundred codes above thr (the one-code bins).  Each
+    against the oracle, with and without group maxima."""
+    _say("topk block-max split wide code offsets")
+    g = np.random.default_rng(77)
+    ulp = np.finfo(np.float32).eps                      # one ulp in [1, 2)
+    for n, k, ns, nl in ((1 << 16, 64, 0, 0), (1 << 18, 300, 128, 256), (64 * 1000, 17, 64, 64)):
+        keys = np.empty((2, n), np.float32)
+        keys[0] = (g.standard_normal(n) - 30.0).astype(np.float32)
+        a = int(g.integers(ns, n - nl - 4 * k))
+        keys[0, a:a + 4 * k] = np.abs(keys[0, a:a + 4 * k]) * 0.25   # 4k positive keys in k/16 blocks
+        keys[1] = np.float32(1.5) + np.arange(n, dtype=np.float32) * ulp
+        g.shuffle(keys[1])
+        kt = dev(keys)
+        bm = kt.view(2, n // 64, 64).amax(-1).contiguous()
+        ref = _topk_ref(keys, k, ns, nl, True)
+        got = host(sdq.topk_select_block_max_split(kt, bm, k, ns, nl, group_max=_groups_of(bm)))
+        assert np.array_equal(got, ref), (n, k, ns, nl)
+        got = host(sdq.topk_select_block_max_split(kt, bm, k, ns, nl))
+        assert np.array_equal(got, ref), (n, k, ns, nl, "no groups")
+
+
 def test_topk_block_max_split_workspace_reuse(sdq):
     """Calls in a row on one split workspace, fewer rows than it was sized
     for, rows that take the exact row path in between: every call is exact
