@@ -705,8 +705,9 @@ def offload_steps(torch, lib, bytemodel, dev, index, q, var, q3, K4, V4, n, G, H
 def fathom_small_step(torch, np, lib, bytemodel, synth, dev, cfg):
     """The bit-plane decode step at config 1 (1 KV head, 4096 tokens, B=48,
     k=64) or config 2 (8 KV heads x 4 query heads, 32768 tokens, B=56, k=512):
-    fused plan + scan, block-max top-k (the generic top-k for config 1, whose
-    competition range is too short for it), gather attention."""
+    fused plan + scan, top-k, gather attention.  Both take the generic top-k:
+    the block-max forms need k well below the row's block count, and at 4096
+    and 32768 tokens k is 1/64 of the row or more."""
     cc = synth.fathom_case(cfg)
     G, Hgrp, n, k, B = cc["G"], cc["Hgrp"], cc["n"], cc["k"], cc["budget"]
     K = torch.from_numpy(cc["K"].view(np.int16)).to(dev)
@@ -722,7 +723,7 @@ def fathom_small_step(torch, np, lib, bytemodel, synth, dev, cfg):
     ws = lib.attend_workspace(1, G * Hgrp, G, False, k, 1, dev)
     ws_t = lib.topk_workspace(G, n, k, lib.SDQ_KEY_F32_MAX, dev)
     K4, V4 = K.view(1, G, n, 128), V.view(1, G, n, 128)
-    use_bm = n - 0 >= 65536
+    use_bm = n >= 65536                          # never at configs 1 and 2
 
     def step(i):
         lib.fathom_plan_scan(index, q, var, B, n, scores=scores, block_max=bm, write_plan=False)
