@@ -45,6 +45,8 @@ constexpr int kTok = 32;                 // tokens per lane (one plane word)
 constexpr int kGroupBlocks = SDQ_GROUP_BLOCKS;   // 64-token blocks per group maximum
 static_assert(kGroupBlocks == 8, "a group is the 16 words of a quarter wave");
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 template <int T>
 struct ChanData {
   uint32_t mw;          // scale | offset << 16
@@ -70,18 +72,33 @@ __device__ __forceinline__ void load_chan(ChanData<T>& d, const ScanSrc& src, in
     d.W[p] = __builtin_amdgcn_raw_buffer_load_b32(src.planes, src.plane_off, base + uint32_t(p) * src.row_bytes, 0);
 }
 
+// (a & m) | (b & ~m) as one v_bfi_b32, kept as written (left to itself the
+// compiler rebuilds the selects below as masks and ORs, twice the work).
+__device__ __forceinline__ uint32_t bfi32(uint32_t m, uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(m), "v"(a), "v"(b));
+  return r;
+}
+
 // Adds one channel's contribution to the 32 scores of the lane's word.
 // q2 = qbar_j * 2^(28-t): with the fp16 scale it gives the weight of a t-bit
 // code read as an fp16 denormal (c * 2^-24).
 //
 // Token pair (i, i+16) takes its two t-bit codes from one register: the
 // codes sit at bit `pos` of the low and of the high half, pos = i for pairs
-// 0..7 and i - 8 for pairs 8..15.  Each plane word is shifted once per
-// channel into two copies (one per group of pairs) so that plane p's bit of
-// token i lands at pos + t-1-p; after that a pair costs one AND per plane and
-// two fma_mix.  A half holding c << pos (< 2^11) reads as the fp16 value
-// c * 2^(pos-24) exactly, so acc[i] collects 2^pos times its true sum; the
-// factor is removed once at the end.
+// 0..7 and i - 8 for pairs 8..15.  A half holding c << pos (< 2^11) reads as
+// the fp16 value c * 2^(pos-24) exactly, so acc[i] collects 2^pos times its
+// true sum; the factor is removed once at the end.  A pair costs one AND and
+// two fma_mix.
+//
+// The registers the pairs are cut from: for t = 1 the plane word itself (and
+// a copy shifted down by 8 for pairs 8..15).  For t >= 2 the codes of all
+// tokens i of one residue class i mod S (S = 2 for t = 2, else 4; S >= t, so
+// the codes of one class do not overlap) sit whole at bits [i, i+t) of one
+// register z: bit x of z comes from plane t-1-s, s = (x - class) mod S, that
+// plane pre-shifted so that token x-s lands on x.  Each class register costs
+// t-1 bit selects, so a channel costs about 2S(t-1) + 2t + 16 bit
+// instructions instead of 16t + 2t.
 template <int T>
 __device__ __forceinline__ void use_chan(const ChanData<T>& d, float qv, float qm, float q2,
                                          float& C, float (&acc)[kTok]) {
@@ -90,32 +107,49 @@ __device__ __forceinline__ void use_chan(const ChanData<T>& d, float qv, float q
   C = __builtin_fmaf(off, qv, C);
   C = __builtin_fmaf(sc, qm, C);
   const float w = sc * q2;
-  uint32_t ua[T], ub[T];
-#pragma unroll
-  for (int p = 0; p < T; ++p) {
-    const int sft = T - 1 - p;                  // code bit of plane p
-    ua[p] = d.W[p] << sft;                       // pairs 0..7:  token i -> bit i + sft
-    ub[p] = d.W[p] >> (8 - sft);                 // pairs 8..15: token i -> bit i - 8 + sft
-  }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  auto pair = [&](int i, uint32_t src) {
     const int pos = i < 8 ? i : i - 8;
-    uint32_t x = (i < 8 ? ua[0] : ub[0]) & (0x00010001u << (pos + T - 1));
-#pragma unroll
-    for (int p = 1; p < T; ++p) {
-      x |= (i < 8 ? ua[p] : ub[p]) & (0x00010001u << (pos + T - 1 - p));
-      asm("" : "+v"(x));               // one v_and_or_b32 per plane
-    }
+    uint32_t x = src & (((1u << T) - 1u) * 0x00010001u << pos);
     asm("" : "+v"(x));                 // keep x whole: its halves feed op_sel
     acc[i] = __builtin_fmaf(half_bits_to_f32(x), w, acc[i]);
     acc[i + 16] = __builtin_fmaf(half_bits_to_f32(x >> 16), w, acc[i + 16]);
+  };
+  if constexpr (T == 1) {
+    const uint32_t lo = d.W[0], hi = d.W[0] >> 8;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pair(i, i < 8 ? lo : hi);
+  } else {
+    constexpr int S = T == 2 ? 2 : 4;
+    constexpr uint32_t M0 = S == 2 ? 0x55555555u : 0x11111111u;   // positions of class 0
+    uint32_t A[T], B[T];     // plane p: token x's bit at x + t-1-p (A) and x - 8 + t-1-p (B)
+#pragma unroll
+    for (int p = 0; p < T; ++p) {
+      A[p] = d.W[p] << (T - 1 - p);
+      B[p] = d.W[p] >> (8 - (T - 1 - p));
+    }
+    uint32_t za[S], zb[S];   // class registers for pairs 0..7 (za) and 8..15 (zb)
+#pragma unroll
+    for (int r = 0; r < S; ++r) {
+      uint32_t va = A[0], vb = B[0];           // offset s = t-1 (and s >= t, never read)
+#pragma unroll
+      for (int s = T - 2; s >= 0; --s) {
+        const uint32_t m = M0 << ((r + s) % S);
+        va = bfi32(m, A[T - 1 - s], va);
+        vb = bfi32(m, B[T - 1 - s], vb);
+      }
+      za[r] = va;
+      zb[r] = vb;
+      asm("" : "+v"(za[r]), "+v"(zb[r]));
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pair(i, i < 8 ? za[i % S] : zb[i % S]);
   }
 }
 
-// Loads in flight per lane are what bound this kernel (few waves, small
-// per-lane loads): a ring of D channel buffers keeps D-1 channels' plane words
-// and metadata in flight while one is accumulated.  The ring is indexed with
-// compile-time slots, so its registers never move.
+// A ring of D channel buffers keeps D-1 channels' plane words and metadata in
+// flight while one is accumulated (deeper or shallower rings measured
+// slower).  The ring is indexed with compile-time slots, so its registers
+// never move.
 template <int T>
 struct RingDepth {
   static constexpr int D = T == 1 ? 6 : (T == 2 ? 4 : 3);
@@ -124,10 +158,10 @@ struct RingDepth {
 // The channels of depth T at list slots a, a + S, a + 2S, ... below end (S = 1,
 // or the number of waves sharing a tile, each taking every S-th channel).
 // Full turns of the ring are straight-line code (D accumulations, each
-// followed by the refill of its slot), so the compiler keeps the refills
-// where they are written and its waits stay exact; refills past the end
-// re-read the run's last channel (an L1 hit).  The last partial turn only
-// drains the ring.
+// followed by the refill of its slot and a scheduling barrier), so the
+// refills stay where they are written and each accumulation waits only for
+// its own slot; refills past the end re-read the run's last channel (an L1
+// hit).  The last partial turn only drains the ring.
 template <int T, int S>
 __device__ __forceinline__ void accum_run(int a, int end, const int* s_j, const float* s_q,
                                           const float* s_qm, const float* s_q2,
@@ -150,6 +184,10 @@ __device__ __forceinline__ void accum_run(int a, int end, const int* s_j, const 
       const int x = a + k * S;
       use_chan<T>(ring[k], s_q[x], s_qm[x], s_q2[x], C, acc);
       fetch(ring[k], x + D * S);
+      // Without this the scheduler hoists the bit work of every slot to the
+      // top of the turn, which waits for all of the ring's loads and drains
+      // it; with it a slot waits only for its own loads.
+      __builtin_amdgcn_sched_barrier(0);
     }
     a += D * S;
   }
@@ -286,9 +324,26 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
   const int r2 = __builtin_amdgcn_readfirstlane(s_run[2]), r3 = __builtin_amdgcn_readfirstlane(s_run[3]);
   constexpr int S = SPLIT ? kScanWaves : 1;
   const int v = SPLIT ? wave : 0;
+  // A CU runs four workgroups at once and its arbiter favours the oldest
+  // waves, so left alone the youngest workgroup does most of its work last,
+  // nearly alone.  Each wave lowers its priority as its share of the work
+  // (about t+2 units per channel of depth t) passes a quarter, a half and
+  // three quarters, so lagging waves go first and the CU's waves end closer
+  // together (measured 0.2-0.4 us faster at 2^20 tokens).
+  const int work = (r1 - r0) * 6 + (r2 - r1) * 5 + (r3 - r2) * 4 + (A - r3) * 3 + 1;
+  auto lower_priority = [&](int done) {
+    const int q = done * 4 / work;
+    if (q == 1) __builtin_amdgcn_s_setprio(2);
+    else if (q == 2) __builtin_amdgcn_s_setprio(1);
+    else if (q >= 3) __builtin_amdgcn_s_setprio(0);
+  };
+  __builtin_amdgcn_s_setprio(3);
   accum_run<4, S>(r0 + v, r1, s_j, s_q, s_qm, s_q2, src, C, acc);
+  lower_priority((r1 - r0) * 6);
   accum_run<3, S>(r1 + v, r2, s_j, s_q, s_qm, s_q2, src, C, acc);
+  lower_priority((r1 - r0) * 6 + (r2 - r1) * 5);
   accum_run<2, S>(r2 + v, r3, s_j, s_q, s_qm, s_q2, src, C, acc);
+  lower_priority((r1 - r0) * 6 + (r2 - r1) * 5 + (r3 - r2) * 4);
   accum_run<1, S>(r3 + v, A, s_j, s_q, s_qm, s_q2, src, C, acc);
   if constexpr (SPLIT) {
     // waves 1.. hand their partial sums to wave 0, which adds them in wave
@@ -339,7 +394,11 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
   for (int v = 0; v < kTok / 4; ++v) {
     const int f = v * 64 + lane;                                  // float4 index in the wave's range
     const int word = f >> 3;                                      // 8 float4 per word
-    if (word < nvalid) dst[f] = so[word * 9 + (f & 7)];
+    // non-temporal: the scores are read once, by another kernel, so they
+    // need not stay in this XCD's L2 (measured 0.2-1 us off the launch)
+    if (word < nvalid)
+      __builtin_nontemporal_store(__builtin_bit_cast(f32x4, so[word * 9 + (f & 7)]),
+                                  reinterpret_cast<f32x4*>(&dst[f]));
   }
   if (block_max || group_max) {
     m = fmaxf(m, __shfl_xor(m, 1, 64));                          // the block's two words
