@@ -141,16 +141,25 @@ __device__ __forceinline__ HeadPlan plan_head(const float* __restrict__ q,
       const int m0 = __popcll(b0), m = m0 + __popcll(b1);
       if (h0) lds[__popcll(b0 & lt)] = u0;
       if (h1) lds[m0 + __popcll(b1 & lt)] = u1;
+      // pad to a multiple of 8 with zeros (below every bucket value, so they
+      // count nowhere) and read 8 values per round, loads ahead of compares
+      const int m8 = (m + 7) & ~7;
+      if (l < m8 - m) lds[m + l] = 0u;
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       int gt0 = 0, ge0 = 0, gt1 = 0, ge1 = 0;
-      for (int i = 0; i < m; ++i) {
-        const uint32_t x = lds[i];
-        gt0 += x > u0;
-        ge0 += x >= u0;
-        gt1 += x > u1;
-        ge1 += x >= u1;
+      const uint4* l4 = reinterpret_cast<const uint4*>(lds);
+      for (int i = 0; i < m8 / 4; i += 2) {
+        const uint4 xa = l4[i], xb = l4[i + 1];
+        const uint32_t xs[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          gt0 += xs[k] > u0;
+          ge0 += xs[k] >= u0;
+          gt1 += xs[k] > u1;
+          ge1 += xs[k] >= u1;
+        }
       }
       const uint64_t c0 = __ballot(h0 && gt0 < r && r <= ge0);
       const uint64_t c1 = __ballot(h1 && gt1 < r && r <= ge1);
@@ -159,21 +168,24 @@ __device__ __forceinline__ HeadPlan plan_head(const float* __restrict__ q,
       __builtin_amdgcn_wave_barrier();              // lds is free again
     }
   }
-  int gt = 0;
-#pragma unroll
-  for (int t = 0; t < NT; ++t) gt += wave_count(v0[t] > T) + wave_count(v1[t] > T);
-  const int rem = K - gt;                  // bits to take among those equal to T
-
-  int before0 = 0, total0 = 0, before1 = 0;
+  // Bits above T, and the bits equal to T in (j, t) order, counted with one
+  // packed wave scan: per lane (#gain > T) | (#gain == T of channel l) << 10
+  // | (#gain == T of channel l+64) << 20, each field below 2^10.
+  int cg = 0, ce0 = 0, ce1 = 0;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const uint64_t e0 = __ballot(K > 0 && v0[t] == T);
-    before0 += __popcll(e0 & lt);
-    total0 += __popcll(e0);
+    cg += int(v0[t] > T) + int(v1[t] > T);
+    ce0 += int(v0[t] == T);
+    ce1 += int(v1[t] == T);
   }
-#pragma unroll
-  for (int t = 0; t < NT; ++t) before1 += __popcll(__ballot(K > 0 && v1[t] == T) & lt);
-  before1 += total0;
+  const int packed = K > 0 ? (cg | ce0 << 10 | ce1 << 20) : 0;
+  const int inc = wave_incl_scan(packed);
+  const int tot = wave_last(inc);
+  const int excl = inc - packed;
+  const int gt = tot & 0x3FF;
+  const int rem = K - gt;                  // bits to take among those equal to T
+  const int before0 = (excl >> 10) & 0x3FF;
+  const int before1 = ((tot >> 10) & 0x3FF) + ((excl >> 20) & 0x3FF);
 
   int d0 = 0, d1 = 0, r0 = before0, r1 = before1;
 #pragma unroll

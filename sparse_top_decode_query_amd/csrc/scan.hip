@@ -223,11 +223,8 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
     PlanIn pin) {
   __shared__ float s_q2[kHeadDim];
   __shared__ int s_j[kHeadDim];
-  __shared__ int s_t[kHeadDim];
   __shared__ float s_q[kHeadDim];
   __shared__ float s_qm[kHeadDim];
-  __shared__ float s_qbar[kHeadDim];
-  __shared__ int s_A;
   __shared__ int s_run[5];          // list slots where depth 4, 3, 2, 1 start; s_run[4] = A
   // each wave's 2048 scores in token order (rows of 32 padded to 36 floats)
   __shared__ float4 s_out[kScanWaves][64 * 9];
@@ -238,12 +235,13 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
   if (wave == 0) {
     // active channels sorted by depth (4 first); depths outside 1..4 are unread
     int t0, t1;
+    float qv0, qv1;
     if constexpr (MODE == 0) {
       // depth and qbar in one round trip
       t0 = depth[size_t(g) * kHeadDim + lane];
       t1 = depth[size_t(g) * kHeadDim + lane + 64];
-      s_qbar[lane] = qbar[size_t(g) * kHeadDim + lane];
-      s_qbar[lane + 64] = qbar[size_t(g) * kHeadDim + lane + 64];
+      qv0 = qbar[size_t(g) * kHeadDim + lane];
+      qv1 = qbar[size_t(g) * kHeadDim + lane + 64];
     } else {
       // s_out is not used before the scores, so it lends the plan its scratch
       // (384 words)
@@ -251,8 +249,8 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
                                               reinterpret_cast<uint32_t*>(&s_out[0][0]));
       t0 = p.d0;
       t1 = p.d1;
-      s_qbar[lane] = p.a0;
-      s_qbar[lane + 64] = p.a1;
+      qv0 = p.a0;
+      qv1 = p.a1;
       if (blockIdx.x == 0 && pin.depth_out) {
         pin.depth_out[size_t(g) * kHeadDim + lane] = uint8_t(t0);
         pin.depth_out[size_t(g) * kHeadDim + lane + 64] = uint8_t(t1);
@@ -260,39 +258,38 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
         pin.qbar_out[size_t(g) * kHeadDim + lane + 64] = p.a1;
       }
     }
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int base = 0;
-    for (int L = 4; L >= 1; --L) {
-      if (lane == 0) s_run[4 - L] = base;
-      const uint64_t b0 = __ballot(t0 == L), b1 = __ballot(t1 == L);
-      if (t0 == L) {
-        const int pos = base + __popcll(b0 & lt);
-        s_j[pos] = lane;
-        s_t[pos] = L;
-      }
-      if (t1 == L) {
-        const int pos = base + __popcll(b0) + __popcll(b1 & lt);
-        s_j[pos] = lane + 64;
-        s_t[pos] = L;
-      }
-      base += __popcll(b0) + __popcll(b1);
-    }
+    // Slots of the active channels, sorted by depth (4 first) and within a
+    // depth by channel, from two packed wave scans: byte 4-L of x0 (x1)
+    // counts channel lane (lane + 64) at depth L.
+    const int x0 = (t0 >= 1 && t0 <= 4) ? 1 << (8 * (4 - t0)) : 0;
+    const int x1 = (t1 >= 1 && t1 <= 4) ? 1 << (8 * (4 - t1)) : 0;
+    const int i0 = wave_incl_scan(x0), i1 = wave_incl_scan(x1);
+    const uint32_t n0 = uint32_t(wave_last(i0)), n1 = uint32_t(wave_last(i1));
+    // byte f of pre: channels in runs 0..f (depth 4..4-f); at most 128, so
+    // the byte-wise sums never carry
+    const uint32_t pre = (n0 + n1) * 0x01010101u;
+    auto place = [&](int t, int j, int before, float qv) {
+      const int f = 4 - t;                       // run of depth t
+      const int run0 = f == 0 ? 0 : int((pre >> (8 * (f - 1))) & 0xFFu);
+      const int slot = run0 + (j >= 64 ? int((n0 >> (8 * f)) & 0xFFu) : 0) +
+                       ((before >> (8 * f)) & 0xFF);
+      s_j[slot] = j;
+      s_q[slot] = qv;
+      s_qm[slot] = qv * (float((1 << (4 - t)) - 1) * 0.5f);
+      s_q2[slot] = qv * float(1u << (28 - t));
+    };
+    if (x0) place(t0, lane, i0 - x0, qv0);
+    if (x1) place(t1, lane + 64, i1 - x1, qv1);
     if (lane == 0) {
-      s_A = base;
-      s_run[4] = base;
+      s_run[0] = 0;
+      s_run[1] = int(pre & 0xFFu);
+      s_run[2] = int((pre >> 8) & 0xFFu);
+      s_run[3] = int((pre >> 16) & 0xFFu);
+      s_run[4] = int(pre >> 24);                 // A
     }
   }
   __syncthreads();
-  const int A = __builtin_amdgcn_readfirstlane(s_A);
-  if (tid < A) {
-    const int j = s_j[tid];
-    const float qv = s_qbar[j];
-    const float half_gap = float((1 << (4 - s_t[tid])) - 1) * 0.5f;
-    s_q[tid] = qv;
-    s_qm[tid] = qv * half_gap;
-    s_q2[tid] = qv * float(1u << (28 - s_t[tid]));
-  }
-  __syncthreads();
+  const int A = __builtin_amdgcn_readfirstlane(s_run[4]);
 
   const size_t nw = size_t(nb64) * 2;                            // words scored (n rounded up to 64)
   const size_t nw_cap = size_t(n_cap) / 32;                       // words per plane row
