@@ -360,7 +360,7 @@ def main():
     # figure a kernel trace averages); and its fixed cost: the same launch with
     # an empty plan (budget 0) over one 64-token block per KV head, i.e.
     # dispatch, the plan and the drain, with nothing to stream
-    scan_launch_us = timeit_graph(torch, plan_scan, reps=64, warm=5)
+    scan_launch_us = timeit_graph(torch, plan_scan, reps=64, warm=5, replays=7)
     sc_small = torch.empty(G, 64, device=dev)
     bm_small = torch.empty(G, 1, device=dev)
     gm_small = torch.empty(G, 1, device=dev)
@@ -395,7 +395,7 @@ def main():
         "traffic": scan_traffic(plan_key),
         "kernel": "fathom_plan_scan", "bytes_per_launch": scan_bytes,
         "launch_us": round(scan_launch_us, 2),
-        "launch_timing": "mean of 64 back-to-back launches (one replayed HIP graph) over the 8 rotating index copies",
+        "launch_timing": "mean of 64 back-to-back launches (a replayed HIP graph) over the 8 rotating index copies, median of 7 replays",
         "trace_avg_us": trace_average(TRACE_FILE, "fathom_scan_kernel<1, false>"),
         "floor_us": round(max(t_hbm, t_valu) * 1e6, 2),
         "frac_of_binding_floor": round(max(t_hbm, t_valu) / scan_s, 4),
@@ -419,8 +419,9 @@ def main():
     plain_us = timeit_graph(torch, lambda i: lib.fathom_scan(index, depth, qbar, n, planes=P[i % N_COPIES],
                                                              meta=M[i % N_COPIES], scores=scores,
                                                              block_max=bmax, group_max=gmax),
-                            reps=64, warm=5)
-    plan_us = timeit_graph(torch, lambda i: lib.fathom_plan(q, var, B, depth=depth, qbar=qbar), reps=64, warm=5)
+                            reps=64, warm=5, replays=7)
+    plan_us = timeit_graph(torch, lambda i: lib.fathom_plan(q, var, B, depth=depth, qbar=qbar), reps=64, warm=5,
+                           replays=7)
     roofline_plain = {"kernel": "fathom_scan (plan read)", "launch_us": round(plain_us, 2),
                       "frac": round(scan_bytes / (plain_us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
                       "fathom_plan_launch_us": round(plan_us, 2)}
@@ -500,13 +501,14 @@ def timeit(torch, fn, reps=30, warm=3, cover=None):
     return e0.elapsed_time(e1) * 1e3 / reps
 
 
-def timeit_graph(torch, fn, reps=30, warm=3):
+def timeit_graph(torch, fn, reps=30, warm=3, replays=1):
     """Mean GPU time per call of `reps` calls captured into one HIP graph and
-    replayed between two events.  A replay launches every captured kernel
-    from the device-side graph, so calls shorter than their host-side launch
-    cost (a Python call through ctypes) are timed back to back, as a decode
-    loop replaying a captured step runs them.  The calls must allocate
-    nothing and must not synchronise."""
+    replayed between two events (the median over `replays` replays).  A
+    replay launches every captured kernel from the device-side graph, so
+    calls shorter than their host-side launch cost (a Python call through
+    ctypes) are timed back to back, as a decode loop replaying a captured
+    step runs them.  The calls must allocate nothing and must not
+    synchronise."""
     for i in range(warm):
         fn(i)
     torch.cuda.synchronize()
@@ -516,13 +518,16 @@ def timeit_graph(torch, fn, reps=30, warm=3):
             fn(i)
     g.replay()                                   # untimed first replay
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    g.replay()
-    e1.record()
-    torch.cuda.synchronize()
+    times = []
+    for _ in range(replays):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3 / reps)
     del g
-    return e0.elapsed_time(e1) * 1e3 / reps
+    return statistics.median(times)
 
 
 def run_extras(torch, np, lib, bytemodel, synth, dev, case, K4, V4, q, var, q3, index, P, M, n, G,

@@ -228,7 +228,20 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
   __shared__ int s_run[5];          // list slots where depth 4, 3, 2, 1 start; s_run[4] = A
   // each wave's 2048 scores in token order (rows of 32 padded to 36 floats)
   __shared__ float4 s_out[kScanWaves][64 * 9];
-  const int g = blockIdx.y;
+  // Which head and tile this workgroup takes.  The dispatcher hands
+  // consecutive workgroups to successive CUs, so with one head per grid row
+  // each CU would hold the same tile of heads of one parity (0, 2, 4, 6 or
+  // 1, 3, 5, 7 at 2^20 tokens), and one such set measured 6 us slower than
+  // the other.  Instead, in every other pair of grid rows the two heads
+  // swap, and each pair's tiles rotate by a quarter row, so a CU's
+  // workgroups mix heads and token ranges (2^20 tokens: 0.2, 0.9 and 1.8 us
+  // faster at B = 47, 56 and 92).  Short rows keep the plain order.
+  int g = blockIdx.y, bx = blockIdx.x;
+  if constexpr (!SPLIT) {
+    const int r = g >> 1;
+    if ((r & 1) && (g ^ 1) < int(gridDim.y)) g ^= 1;
+    bx = int((unsigned(bx) + unsigned(r) * (gridDim.x >> 2)) % gridDim.x);
+  }
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
 
@@ -251,7 +264,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
       t1 = p.d1;
       qv0 = p.a0;
       qv1 = p.a1;
-      if (blockIdx.x == 0 && pin.depth_out) {
+      if (bx == 0 && pin.depth_out) {
         pin.depth_out[size_t(g) * kHeadDim + lane] = uint8_t(t0);
         pin.depth_out[size_t(g) * kHeadDim + lane + 64] = uint8_t(t1);
         pin.qbar_out[size_t(g) * kHeadDim + lane] = p.a0;
@@ -293,7 +306,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
 
   const size_t nw = size_t(nb64) * 2;                            // words scored (n rounded up to 64)
   const size_t nw_cap = size_t(n_cap) / 32;                       // words per plane row
-  const int tile = SPLIT ? int(blockIdx.x) : int(blockIdx.x) * kScanWaves + wave;
+  const int tile = SPLIT ? bx : bx * kScanWaves + wave;
   const int wd = tile * 64 + lane;                                // this lane's 32-token word
   if (tile * 64 >= int(nw)) return;                               // whole wave past the end
   const bool valid = wd < int(nw);
