@@ -145,6 +145,37 @@ def test_fused_plan_scan_1m_all_heads(layer, budget, uniform):
     assert float(np.abs(host(out) - ref_o).max()) <= ATTN_ATOL
 
 
+@pytest.mark.parametrize("G,n", [(3, (1 << 20) - 27), (4, (1 << 20) - 27), (6, (1 << 20) - 1000)],
+                         ids=["G3", "G4", "G6"])
+def test_fused_plan_scan_long_rows_head_subsets(layer, G, n):
+    """Long rows over the first G KV heads of the layer, n below the row
+    capacity (the open block partly filled), in the one-wave-per-tile grid
+    with its head swap and tile rotation (an odd head count leaves the last
+    row unswapped): plan and all G score rows against the oracle; block
+    maxima exact; tokens past n score -inf."""
+    lib, case, n_cap = layer["lib"], layer["case"], layer["n"]
+    _say(f"fused plan + scan over heads 0..{G - 1}, n={n}, n_cap={n_cap}")
+    planes = layer["index"].planes[:G]
+    meta = layer["index"].meta[:G]
+    sub = lib.PlaneIndex(planes, meta)
+    n64 = -(-n // 64) * 64
+    bm = torch.empty(G, n64 // 64, device="cuda")
+    depth, qbar, scores = lib.fathom_plan_scan(sub, layer["q"][:G * 4], layer["var"][:G], 56, n,
+                                               block_max=bm)
+    torch.cuda.synchronize()
+    q_np, var_np = case["q"][:G * 4], case["var"][:G]
+    rd, rq = o_fathom.plan_heads(q_np, var_np, 4, budget=56)
+    assert np.array_equal(host(depth), rd) and np.array_equal(host(qbar), rq)
+    rp, rm = layer["rp"][:G], layer["rm"][:G]
+    with ThreadPoolExecutor(G) as ex:
+        ref = np.stack(list(ex.map(lambda g: o_fathom.scan(rp[g], rm[g], rd[g], rq[g], n), range(G))))
+    S = host(scores)
+    assert S.shape == (G, n64)
+    assert np.all(np.isneginf(S[:, n:]))
+    _assert_rows(S[:, :n], ref)
+    assert np.array_equal(host(bm), S.reshape(G, n64 // 64, 64).max(axis=2))
+
+
 def test_offload_gather_1m_against_oracle(layer):
     """The offloaded setting at full size: the whole index sits in pinned host
     memory and fathom_gather, on a side stream ordered by events, copies the
