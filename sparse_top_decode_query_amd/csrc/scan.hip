@@ -163,15 +163,14 @@ struct RingDepth {
 // its own slot; refills past the end re-read the run's last channel (an L1
 // hit).  The last partial turn only drains the ring.
 template <int T, int S>
-__device__ __forceinline__ void accum_run(int a, int end, const int* s_j, const float* s_q,
-                                          const float* s_qm, const float* s_q2,
+__device__ __forceinline__ void accum_run(int a, int end, const float4* s_ch,
                                           const ScanSrc& src, float& C, float (&acc)[kTok]) {
   constexpr int D = RingDepth<T>::D;
   if (a >= end) return;
   const int last = a + (end - 1 - a) / S * S;        // the last slot this wave takes
   auto fetch = [&](ChanData<T>& d, int x) {
     x = x < last ? x : last;
-    load_chan<T>(d, src, __builtin_amdgcn_readfirstlane(s_j[x]));
+    load_chan<T>(d, src, __builtin_amdgcn_readfirstlane(__float_as_int(s_ch[x].w)));
   };
   ChanData<T> ring[D];
 #pragma unroll
@@ -182,7 +181,8 @@ __device__ __forceinline__ void accum_run(int a, int end, const int* s_j, const 
 #pragma unroll
     for (int k = 0; k < D; ++k) {
       const int x = a + k * S;
-      use_chan<T>(ring[k], s_q[x], s_qm[x], s_q2[x], C, acc);
+      const float4 ch = s_ch[x];
+      use_chan<T>(ring[k], ch.x, ch.y, ch.z, C, acc);
       fetch(ring[k], x + D * S);
       // Without this the scheduler hoists the bit work of every slot to the
       // top of the turn, which waits for all of the ring's loads and drains
@@ -195,7 +195,10 @@ __device__ __forceinline__ void accum_run(int a, int end, const int* s_j, const 
 #pragma unroll
   for (int k = 0; k < D; ++k) {
     const int x = a + k * S;
-    if (k < rem) use_chan<T>(ring[k], s_q[x], s_qm[x], s_q2[x], C, acc);
+    if (k < rem) {
+      const float4 ch = s_ch[x];
+      use_chan<T>(ring[k], ch.x, ch.y, ch.z, C, acc);
+    }
   }
 }
 
@@ -221,10 +224,10 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
     const uint8_t* __restrict__ depth, const float* __restrict__ qbar, int n, int nb64, int n_cap,
     float* __restrict__ scores, float* __restrict__ block_max, float* __restrict__ group_max,
     PlanIn pin) {
-  __shared__ float s_q2[kHeadDim];
-  __shared__ int s_j[kHeadDim];
-  __shared__ float s_q[kHeadDim];
-  __shared__ float s_qm[kHeadDim];
+  // the active channels in depth order (4 first): qbar_j, its offset weight,
+  // its code weight (see use_chan) and the channel index j, one 16-byte
+  // read a channel
+  __shared__ float4 s_ch[kHeadDim];
   __shared__ int s_run[5];          // list slots where depth 4, 3, 2, 1 start; s_run[4] = A
   // each wave's 2048 scores in token order (rows of 32 padded to 36 floats)
   __shared__ float4 s_out[kScanWaves][64 * 9];
@@ -286,10 +289,8 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
       const int run0 = f == 0 ? 0 : int((pre >> (8 * (f - 1))) & 0xFFu);
       const int slot = run0 + (j >= 64 ? int((n0 >> (8 * f)) & 0xFFu) : 0) +
                        ((before >> (8 * f)) & 0xFF);
-      s_j[slot] = j;
-      s_q[slot] = qv;
-      s_qm[slot] = qv * (float((1 << (4 - t)) - 1) * 0.5f);
-      s_q2[slot] = qv * float(1u << (28 - t));
+      s_ch[slot] = make_float4(qv, qv * (float((1 << (4 - t)) - 1) * 0.5f),
+                               qv * float(1u << (28 - t)), __int_as_float(j));
     };
     if (x0) place(t0, lane, i0 - x0, qv0);
     if (x1) place(t1, lane + 64, i1 - x1, qv1);
@@ -348,13 +349,13 @@ __global__ __launch_bounds__(kScanWaves * 64) void fathom_scan_kernel(
     else if (q >= 3) __builtin_amdgcn_s_setprio(0);
   };
   __builtin_amdgcn_s_setprio(3);
-  accum_run<4, S>(r0 + v, r1, s_j, s_q, s_qm, s_q2, src, C, acc);
+  accum_run<4, S>(r0 + v, r1, s_ch, src, C, acc);
   lower_priority((r1 - r0) * 6);
-  accum_run<3, S>(r1 + v, r2, s_j, s_q, s_qm, s_q2, src, C, acc);
+  accum_run<3, S>(r1 + v, r2, s_ch, src, C, acc);
   lower_priority((r1 - r0) * 6 + (r2 - r1) * 5);
-  accum_run<2, S>(r2 + v, r3, s_j, s_q, s_qm, s_q2, src, C, acc);
+  accum_run<2, S>(r2 + v, r3, s_ch, src, C, acc);
   lower_priority((r1 - r0) * 6 + (r2 - r1) * 5 + (r3 - r2) * 4);
-  accum_run<1, S>(r3 + v, A, s_j, s_q, s_qm, s_q2, src, C, acc);
+  accum_run<1, S>(r3 + v, A, s_ch, src, C, acc);
   if constexpr (SPLIT) {
     // waves 1.. hand their partial sums to wave 0, which adds them in wave
     // order (the staging rows of waves 1.. are free until then)
