@@ -895,8 +895,9 @@ __global__ __launch_bounds__(kU8SegThreads) void topk_u8_hist_kernel(const uint8
 // range computes its tokens' distances popcount(sig XOR qsig), stores them,
 // and writes the segment's 256-bin histogram in the layout
 // topk_u8_hist_kernel writes.  A distance lies in [0, 32], so only 33 bins
-// are counted (in LDS, privatised per wave and lane quarter, odd row stride
-// so that one bin's copies fall in different banks) and the rest are zero.
+// are counted (in LDS, privatised per wave and per lane sixteenth, odd row
+// stride so that one bin's copies fall in different banks: a bin's LDS
+// atomics meet at most 4 lanes of a wave) and the rest are zero.
 // 1024 threads of 16 tokens cover one segment.  One more workgroup per row
 // stores the distances of the sink and local windows [0, lo) and [hi, n).
 // Signature rows are n_cap long.
@@ -904,11 +905,12 @@ constexpr int kHhThreads = 1024;
 constexpr int kHhPer = kU8Seg / kHhThreads;                // 16 tokens per thread
 constexpr int kHhBins = 33;
 constexpr int kHhWaves = kHhThreads / 64;
+constexpr int kHhCopies = 16;                              // histogram copies per wave
 
 __global__ __launch_bounds__(kHhThreads) void hamming_hist_kernel(
     const uint32_t* __restrict__ sigs, const uint32_t* __restrict__ qsig, int n, int n_cap, int lo,
     int hi, int nseg, uint8_t* __restrict__ dist, uint32_t* __restrict__ ws) {
-  __shared__ uint32_t h[kHhWaves * 4][kHhBins];
+  __shared__ uint32_t h[kHhWaves * kHhCopies][kHhBins];
   const int seg = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
   const uint32_t qs = qsig[row];
   const uint32_t* srow = sigs + size_t(row) * n_cap;
@@ -918,8 +920,8 @@ __global__ __launch_bounds__(kHhThreads) void hamming_hist_kernel(
     for (int i = hi + tid; i < n; i += kHhThreads) drow[i] = uint8_t(__popc(srow[i] ^ qs));
     return;
   }
-  const int copy = (tid >> 6) * 4 + (tid & 3);
-  for (int i = tid; i < kHhWaves * 4 * kHhBins; i += kHhThreads) (&h[0][0])[i] = 0;
+  const int copy = (tid >> 6) * kHhCopies + (tid & (kHhCopies - 1));
+  for (int i = tid; i < kHhWaves * kHhCopies * kHhBins; i += kHhThreads) (&h[0][0])[i] = 0;
   const int s = lo + seg * kU8Seg + tid * kHhPer;
   const int e = s + kHhPer < hi ? s + kHhPer : hi;
   const int cnt = e > s ? e - s : 0;
@@ -957,17 +959,20 @@ __global__ __launch_bounds__(kHhThreads) void hamming_hist_kernel(
   for (int i = 0; i < kHhPer; ++i)
     if (i < cnt) atomicAdd(&h[copy][(dw[i >> 2] >> (8 * (i & 3))) & 0xFFu], 1u);
   __syncthreads();
-  // each wave's four copies into its first, then the waves' sums per bin
+  // each wave's copies into its first, then the waves' sums per bin
   if (tid < kHhWaves * kHhBins) {
     const int w = tid / kHhBins, bin = tid - w * kHhBins;
-    h[4 * w][bin] += h[4 * w + 1][bin] + h[4 * w + 2][bin] + h[4 * w + 3][bin];
+    uint32_t t = 0;
+#pragma unroll
+    for (int c = 0; c < kHhCopies; ++c) t += h[kHhCopies * w + c][bin];
+    h[kHhCopies * w][bin] = t;
   }
   __syncthreads();
   if (tid < 256) {
     uint32_t t = 0;
     if (tid < kHhBins) {
 #pragma unroll
-      for (int w = 0; w < kHhWaves; ++w) t += h[4 * w][tid];
+      for (int w = 0; w < kHhWaves; ++w) t += h[kHhCopies * w][tid];
     }
     ws[(size_t(row) * nseg + seg) * 256 + tid] = t;
   }
