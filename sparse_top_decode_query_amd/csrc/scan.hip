@@ -12,12 +12,13 @@
 // plane row is read as 64 consecutive dwords per wave (256-byte coalesced
 // vector loads, each byte once), and the lane's 32 tokens share one 64-token
 // block, so the weights w_bj are per-lane values.  Tokens i and i+16 of the
-// word are handled together: one AND per plane moves their t-bit codes into
-// the low and high 16-bit halves of one register, and a code pattern c read as
-// an fp16 is the denormal c * 2^-24 -- exact -- so one v_fma_mix_f32 per token
-// and channel adds c * (w_bj * 2^(24+4-t)) to a float32 accumulator.  That is
-// (t+2)/2 instructions per token and channel instead of one extract and one
-// multiply-add per bit.  The float32 constant C_b is accumulated alongside.
+// word are handled together: one AND moves their t-bit codes into the low and
+// high 16-bit halves of one register (cut from per-channel code registers,
+// see use_chan), and a code pattern c read as an fp16 is the denormal
+// c * 2^-24 -- exact -- so one v_fma_mix_f32 per token and channel adds
+// c * (w_bj * 2^(24+4-t)) to a float32 accumulator: about 1.5 instructions
+// per token and channel instead of one extract and one multiply-add per bit.
+// The float32 constant C_b is accumulated alongside.
 //
 // Each channel's metadata and plane words come from a ring of buffers, three
 // to six channels deep, to keep loads in flight.  Scores leave through LDS:
