@@ -310,7 +310,7 @@ def _topk_ref(keys, k, n_sink, n_local, largest):
                                             (2, 5000, 512, 3, 17), (1, 1000, 2000, 0, 0),
                                             (2, 70001, 512, 0, 0), (8, 1 << 20, 512, 0, 0),
                                             (2, 200000, 3000, 128, 128), (3, 300, 0, 5, 5),
-                                            (8, 32768, 512, 0, 0), (2, 32788, 300, 10, 10),
+                                            (8, 32768, 512, 0, 0), (3, 28672, 585, 0, 0), (2, 32788, 300, 10, 10),
                                             (2, 32809, 100, 20, 20), (3, 40000, 2000, 0, 0),
                                             (2, 16384, 16383, 0, 0), (1, 32768, 32768, 0, 0),
                                             (2, 1025, 1024, 0, 0), (4, 1500, 100, 0, 0),
@@ -350,6 +350,14 @@ def test_topk_f32_degenerate_rows(sdq):
         for k2 in (1, 512, n2 - 1):
             got = host(sdq.topk_select(dev(keys), k2, 0, 0))
             assert np.array_equal(got, _topk_ref(keys, k2, 0, 0, True)), (n2, k2)
+    # rows split into 4096-key segments whose winners are united: keys drawn
+    # from 50 values (ties inside and across segments), 7 and 8 segments
+    rng = np.random.default_rng(7)
+    for n2, k2 in ((32768, 512), (32768, 3), (28672, 585)):
+        keys = rng.integers(0, 50, size=(3, n2)).astype(np.float32)
+        keys[2, ::4096] = 60.0                     # each segment's first key above the rest
+        got = host(sdq.topk_select(dev(keys), k2, 0, 0))
+        assert np.array_equal(got, _topk_ref(keys, k2, 0, 0, True)), (n2, k2)
 
 
 @pytest.mark.parametrize("rows,n,k,ns,nl", [(8, 1 << 20, 512, 0, 0), (2, 65536 + 128, 64, 64, 64),
