@@ -148,23 +148,40 @@ __device__ __forceinline__ HeadPlan plan_head(const float* __restrict__ q,
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      int gt0 = 0, ge0 = 0, gt1 = 0, ge1 = 0;
       const uint4* l4 = reinterpret_cast<const uint4*>(lds);
-      for (int i = 0; i < m8 / 4; i += 2) {
-        const uint4 xa = l4[i], xb = l4[i + 1];
-        const uint32_t xs[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+      if (m <= 64) {
+        // one bucket value a lane (the usual case: 14-26 values at B = 56)
+        const uint32_t x = lds[l];
+        int gt = 0, ge = 0;
+        for (int i = 0; i < m8 / 4; i += 2) {
+          const uint4 xa = l4[i], xb = l4[i + 1];
+          const uint32_t xs[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          gt0 += xs[k] > u0;
-          ge0 += xs[k] >= u0;
-          gt1 += xs[k] > u1;
-          ge1 += xs[k] >= u1;
+          for (int k = 0; k < 8; ++k) {
+            gt += xs[k] > x;
+            ge += xs[k] >= x;
+          }
         }
+        const uint64_t c = __ballot(l < m && gt < r && r <= ge);
+        T = uint32_t(__builtin_amdgcn_readlane(int(x), int(__builtin_ctzll(c))));
+      } else {
+        int gt0 = 0, ge0 = 0, gt1 = 0, ge1 = 0;
+        for (int i = 0; i < m8 / 4; i += 2) {
+          const uint4 xa = l4[i], xb = l4[i + 1];
+          const uint32_t xs[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            gt0 += xs[k] > u0;
+            ge0 += xs[k] >= u0;
+            gt1 += xs[k] > u1;
+            ge1 += xs[k] >= u1;
+          }
+        }
+        const uint64_t c0 = __ballot(h0 && gt0 < r && r <= ge0);
+        const uint64_t c1 = __ballot(h1 && gt1 < r && r <= ge1);
+        T = c0 ? uint32_t(__builtin_amdgcn_readlane(int(u0), int(__builtin_ctzll(c0))))
+               : uint32_t(__builtin_amdgcn_readlane(int(u1), int(__builtin_ctzll(c1))));
       }
-      const uint64_t c0 = __ballot(h0 && gt0 < r && r <= ge0);
-      const uint64_t c1 = __ballot(h1 && gt1 < r && r <= ge1);
-      T = c0 ? uint32_t(__builtin_amdgcn_readlane(int(u0), int(__builtin_ctzll(c0))))
-             : uint32_t(__builtin_amdgcn_readlane(int(u1), int(__builtin_ctzll(c1))));
       __builtin_amdgcn_wave_barrier();              // lds is free again
     }
   }
